@@ -1,0 +1,194 @@
+#!/usr/bin/env python3
+"""Benchmark of the pipelined, persistent tiled GEMM C = A·Bᵀ on one MI355X.
+
+Default workload: M = N = K = 8192, bf16 inputs drawn N(0,1)/sqrt(K), fp32 accumulation, bf16
+output. One step is one gemm_run over operands already resident in HBM. Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--shape-index I]
+                    [--config JSON] [--no-cpu-baseline] [--copy-calibration]
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GEMM TFLOP/s and % of dense fp16/bf16 MFMA peak (8192³ bf16, 1×MI355X)"
+# MI355X dense fp16/bf16 MFMA peak: 256 CUs x 2.4 GHz x 4096 flop/clk/CU (AMD quotes 2.5 PFLOP/s)
+PEAK_TFLOPS = 256 * 2.4e9 * 4096 / 1e12
+PEAK_HBM_GBS = 8000.0
+DTYPE_NAME = {0: "f16", 1: "bf16", 2: "f32"}
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "software_pipelined_tiled_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str, shape_index: int, kernel: str) -> float | None:
+    """HBM bytes per launch from the committed counter summary, if it matches these sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}_{shape_index}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("kernel_source_sha") != kernel_source_hash() or d.get("kernel") != kernel:
+        return None
+    return float(d["hbm_bytes_per_launch"])
+
+
+def cpu_baseline(a_bits, b_bits, K, in_dt, out_dt, seconds: float) -> dict:
+    """The oracle (fp64 triple loop) on the host cores, on a bounded row sample of the workload."""
+    from oracle import oracle as orc
+
+    threads = max(1, min(16, os.cpu_count() or 1))
+    N = b_bits.shape[0]
+    rows = min(2 * threads, a_bits.shape[0])
+    t0 = time.perf_counter()
+    orc.gemm(a_bits[:rows], b_bits, K, in_dt, out_dt, threads=threads, want_sums=False)
+    t_probe = time.perf_counter() - t0
+    rows2 = int(max(rows, min(a_bits.shape[0], rows * seconds / max(t_probe, 1e-3))))
+    rows2 = max(threads, (rows2 // threads) * threads)
+    t0 = time.perf_counter()
+    orc.gemm(a_bits[:rows2], b_bits, K, in_dt, out_dt, threads=threads, want_sums=False)
+    dt = time.perf_counter() - t0
+    return {"value": 2.0 * rows2 * N * K / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"rows 0..{rows2 - 1} of A against all {N} rows of B (K={K}); "
+                      f"{2.0 * rows2 * N * K:.3e} flop in {dt:.2f} s, fp64 triple loop, {threads} threads"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c3_8192_bf16_bf16")
+    ap.add_argument("--shape-index", type=int, default=0)
+    ap.add_argument("--config", default=None, help="JSON kernel-config override (ablations)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also launch one 1 GiB copy kernel (reference for memory-traffic counters)")
+    ap.add_argument("--no-probes", action="store_true", help="skip the MFMA-peak and HBM-copy probes")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures a single GPU: runs with --gpus N for N > 1 are not supported by this build",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import software_pipelined_tiled_amd as spt
+    import synthetic_inputs as si
+
+    torch.cuda.set_device(0)
+    M, N, K, a_bits, b_bits, in_dt, out_dt = si.workload_operands(args.workload, args.shape_index)
+    tdt = {0: torch.float16, 1: torch.bfloat16, 2: torch.float32}
+    A = torch.from_numpy(a_bits.view(np.int16)).cuda().view(tdt[in_dt])
+    B = torch.from_numpy(b_bits.view(np.int16)).cuda().view(tdt[in_dt])
+    C = torch.empty((M, N), dtype=tdt[out_dt], device="cuda")
+    config = json.loads(args.config) if args.config else None
+    plan = spt.Plan(M, N, K, tdt[in_dt], tdt[out_dt], config=config)
+    desc = plan.describe()
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    for _ in range(args.warmup):
+        plan.run_ptrs(A.data_ptr(), B.data_ptr(), C.data_ptr(), sp)
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    all_start, all_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    all_start.record(stream)
+    for i in range(args.steps):
+        starts[i].record(stream)
+        plan.run_ptrs(A.data_ptr(), B.data_ptr(), C.data_ptr(), sp)
+        ends[i].record(stream)
+    all_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+
+    ms_per_step = all_start.elapsed_time(all_end) / args.steps
+    launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    avg_launch_ms = float(np.mean(launch_ms))
+    flop = 2.0 * M * N * K
+    value = flop / (ms_per_step * 1e-3) / 1e12
+    achieved = flop / (avg_launch_ms * 1e-3) / 1e12
+    kernel_name = (f"gemm_{'dma' if desc['load_path'] == 1 else 'reg'}_kernel<{desc['bm']},{desc['bn']},"
+                   f"{desc['bk']},{desc['stages']},{DTYPE_NAME[in_dt]},{DTYPE_NAME[out_dt]}>")
+    traffic = load_traffic(args.workload, args.shape_index, kernel_name)
+    compulsory = (M * K + N * K) * 2 + M * N * (4 if out_dt == 2 else 2)
+
+    extra = {"avg_launch_ms": avg_launch_ms, "min_launch_ms": float(np.min(launch_ms)),
+             "max_launch_ms": float(np.max(launch_ms)), "wall_s": wall,
+             "pct_of_spec_peak": 100.0 * value / PEAK_TFLOPS,
+             "compulsory_hbm_GBps": compulsory / (avg_launch_ms * 1e-3) / 1e9,
+             "kernel_source_sha": kernel_source_hash()}
+
+    if not args.no_probes:
+        iters = 20000
+        pk_s, pk_e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        spt.gemm_probe_mfma_peak(100, 2, sp)
+        pk_s.record(stream)
+        flops = spt.gemm_probe_mfma_peak(iters, 2, sp)
+        pk_e.record(stream)
+        torch.cuda.synchronize()
+        extra["mfma_peak_measured_TFLOPs"] = flops / (pk_s.elapsed_time(pk_e) * 1e-3) / 1e12
+    if args.copy_calibration or not args.no_probes:
+        nbytes = 1 << 30
+        src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        spt.gemm_probe_copy(src.data_ptr(), dst.data_ptr(), nbytes, sp)
+        cs, ce = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        cs.record(stream)
+        spt.gemm_probe_copy(src.data_ptr(), dst.data_ptr(), nbytes, sp)
+        ce.record(stream)
+        torch.cuda.synchronize()
+        extra["copy_probe_GBps"] = 2 * nbytes / (cs.elapsed_time(ce) * 1e-3) / 1e9
+        del src, dst
+
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": DTYPE_NAME[in_dt],
+        "data": "synthetic",
+        "config": {"workload": args.workload, "M": M, "N": N, "K": K, "in_dtype": DTYPE_NAME[in_dt],
+                   "out_dtype": DTYPE_NAME[out_dt], "accumulate": "f32",
+                   "distribution": si.WORKLOADS[args.workload]["dist"], "kernel": kernel_name, "plan": desc},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_TFLOPS, "traffic": traffic},
+        "extra": extra,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(a_bits, b_bits, K, in_dt, out_dt, args.cpu_seconds)
+    plan.close()
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,171 @@
+/*
+ * gemm.h — C ABI of a software-pipelined, persistent, tiled GEMM for AMD Instinct MI355X (gfx950).
+ *
+ *     C = A · Bᵀ      A[M, K] and B[N, K] K-major (row-major with leading dimensions lda, ldb),
+ *                     fp16 or bf16 inputs, fp32 accumulation, C[M, N] row-major (ldc) in fp16,
+ *                     bf16 or fp32.
+ *
+ * The operation is the tiled GEMM of the tutorial "GEMM II — pipelining with TMA" (Step 4: the
+ * A tile at {m, k} and the B tile at {n, k}, fp32 accumulate; Step 5: a ring of stages fed ahead
+ * of the math; Step 6: a persistent pool of workgroups walking a grouped tile raster; the
+ * TMA-store epilogue: cast the fp32 accumulator to the output type and store). The stage ring
+ * follows "Multi-Stage Software Pipelining" (Prefill / Main loop, num_stages 2..4); the operand
+ * staging layout follows the 128-byte swizzle of "Async Data Movement: TMA".
+ *
+ * Element (i, j) of C is  sum_{k<K} A[i*lda + k] * B[j*ldb + k],  accumulated in fp32 and rounded
+ * to nearest-even into the output type. C is overwritten; there is no alpha, beta or bias.
+ *
+ * Ownership and threading.
+ *   - A plan is created by gemm_plan_create, owned by the caller, immutable after creation, and
+ *     freed by gemm_plan_destroy. It holds no device memory.
+ *   - A, B and C are caller-owned device pointers; they must stay valid until the work enqueued
+ *     by gemm_run has completed on its stream.
+ *   - gemm_run only enqueues kernels on `stream` (a hipStream_t; NULL is the default stream). It
+ *     neither allocates nor synchronises, so one plan may be run concurrently on several streams.
+ *
+ * Errors. Every entry point returns a gemm_status_t; nothing aborts or throws across the ABI.
+ * A failed kernel launch returns GEMM_ERR_HIP. Misalignment is never an error: it only selects
+ * the register-staged load path.
+ */
+#ifndef SPT_GEMM_H
+#define SPT_GEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { GEMM_F16 = 0, GEMM_BF16 = 1, GEMM_F32 = 2 } gemm_dtype_t;
+
+typedef enum {
+  GEMM_OK = 0,
+  GEMM_ERR_INVALID = -1,     /* a null out-pointer, negative size, ld too small, bad config */
+  GEMM_ERR_UNSUPPORTED = -2, /* dtype combination or size this library does not handle */
+  GEMM_ERR_HIP = -3,         /* a HIP runtime call or kernel launch failed */
+  GEMM_ERR_NOMEM = -4        /* host allocation of the plan failed */
+} gemm_status_t;
+
+/* How the K-loop stages operand tiles into LDS. */
+typedef enum {
+  GEMM_LOAD_AUTO = 0, /* DMA when pointers, lda/ldb and K allow it, else REG */
+  GEMM_LOAD_DMA = 1,  /* direct global->LDS buffer loads (16-byte chunks, needs alignment) */
+  GEMM_LOAD_REG = 2   /* global->VGPR->LDS copies with per-element K masking (any alignment) */
+} gemm_load_path_t;
+
+/*
+ * Kernel configuration. gemm_plan_create takes an optional override (NULL = heuristic);
+ * gemm_plan_describe reports the configuration a plan will launch.
+ *   bm, bn, bk   output tile (bm x bn) and K-tile depth; bk is 64 or 128
+ *   stages       S, LDS ring depth (1 = serial: wait for a tile, compute it, then load the next)
+ *   waves        wavefronts per workgroup (64 lanes each)
+ *   mfma         MFMA shape: 16 = v_mfma_f32_16x16x32_{f16,bf16}
+ *   persistent   1: launch min(#tiles, grid) workgroups that loop over tiles; 0: one per tile
+ *   group_m      grouped raster height, in tiles (tiles sharing A row bands run back to back)
+ *   load_path    gemm_load_path_t
+ *   grid         workgroups launched (describe only; 0 in an override means "from the device")
+ *   lds_bytes    LDS per workgroup (describe only)
+ */
+typedef struct {
+  int bm, bn, bk;
+  int stages;
+  int waves;
+  int mfma;
+  int persistent;
+  int group_m;
+  int load_path;
+  int grid;
+  int lds_bytes;
+} gemm_config_t;
+
+typedef struct gemm_plan_s* gemm_plan_t;
+
+/*
+ * Create a plan for C[M,N] = A[M,K]·B[N,K]ᵀ on the current HIP device.
+ *   out       receives the plan (set to NULL on failure)
+ *   M, N, K   sizes, each in [0, 2^31 - 1]; M or N == 0 makes gemm_run a no-op, K == 0 writes zeros
+ *   a_dtype, b_dtype   GEMM_F16 or GEMM_BF16, and equal
+ *   c_dtype   GEMM_F16, GEMM_BF16 or GEMM_F32
+ *   lda >= K, ldb >= K, ldc >= N   leading dimensions in elements
+ *   config    NULL for the built-in choice, else an explicit configuration (validated)
+ * Errors: GEMM_ERR_INVALID (null out, bad sizes or ld, invalid override),
+ *         GEMM_ERR_UNSUPPORTED (dtype pair, a tile whose row span exceeds 2^31 bytes),
+ *         GEMM_ERR_HIP (no usable gfx950 device), GEMM_ERR_NOMEM.
+ */
+gemm_status_t gemm_plan_create(gemm_plan_t* out, int64_t M, int64_t N, int64_t K,
+                               gemm_dtype_t a_dtype, gemm_dtype_t b_dtype, gemm_dtype_t c_dtype,
+                               int64_t lda, int64_t ldb, int64_t ldc, const gemm_config_t* config);
+
+/*
+ * Enqueue C = A·Bᵀ on `stream` (hipStream_t, NULL = default stream).
+ *   A: M rows of lda elements, B: N rows of ldb elements, C: M rows of ldc elements; only
+ *   C[i*ldc + j] with i < M, j < N is written (the ldc padding is never touched).
+ *   If A or B is not 16-byte aligned the register-staged path runs instead of the DMA path.
+ * Errors: GEMM_ERR_INVALID (null plan; null A, B or C while M, N > 0), GEMM_ERR_HIP (launch).
+ */
+gemm_status_t gemm_run(gemm_plan_t plan, const void* A, const void* B, void* C, void* stream);
+
+/* Free a plan. NULL is accepted and returns GEMM_OK. */
+gemm_status_t gemm_plan_destroy(gemm_plan_t plan);
+
+/* Copy the configuration `plan` launches into *out. Errors: GEMM_ERR_INVALID on NULL. */
+gemm_status_t gemm_plan_describe(gemm_plan_t plan, gemm_config_t* out);
+
+/* Static, human-readable name of a status code ("GEMM_OK", ...). Never NULL. */
+const char* gemm_status_string(gemm_status_t status);
+
+/* ------------------------------------------------------------------------------------------
+ * Host-only introspection (no device work). They expose the exact functions the kernels use,
+ * so their invariants can be tested without a GPU.
+ * ---------------------------------------------------------------------------------------- */
+
+/*
+ * The configuration gemm_plan_create would choose for this problem on a device with `cu_count`
+ * compute units and `lds_bytes` of LDS per workgroup, assuming 16-byte aligned pointers.
+ * Same argument checks and errors as gemm_plan_create (minus GEMM_ERR_HIP).
+ */
+gemm_status_t gemm_select_config(int64_t M, int64_t N, int64_t K, gemm_dtype_t a_dtype,
+                                 gemm_dtype_t b_dtype, gemm_dtype_t c_dtype, int64_t lda,
+                                 int64_t ldb, int64_t ldc, int cu_count, int lds_bytes,
+                                 gemm_config_t* out);
+
+/*
+ * Output tile handled by workgroup `wg` (0 <= wg < grid) on its `round`-th pass of the
+ * persistent loop, for a tiles_m x tiles_n tile grid, grouped raster of height group_m, and
+ * `grid` workgroups (dispatched round-robin over the 8 XCDs). Writes (*tm, *tn) and returns 1,
+ * or returns 0 when that workgroup has no tile in that round. Invalid arguments return -1.
+ */
+int gemm_schedule_tile(int64_t tiles_m, int64_t tiles_n, int group_m, int grid, int wg, int round,
+                       int64_t* tm, int64_t* tn);
+
+/*
+ * Byte offset, inside one LDS operand tile of `rows` rows and depth bk (64 or 128), of the
+ * 16-byte chunk holding elements [8*chunk, 8*chunk + 8) of tile row `row` (the XOR swizzle).
+ * Returns -1 for invalid arguments.
+ */
+int64_t gemm_lds_chunk_offset(int rows, int bk, int row, int chunk);
+
+/* ------------------------------------------------------------------------------------------
+ * Measurement aids (device work on `stream`; the caller times them with events).
+ * ---------------------------------------------------------------------------------------- */
+
+/*
+ * Launch a dense-MFMA throughput kernel: every wave issues `iters` x 16 independent
+ * v_mfma_f32_16x16x32_bf16 on register operands, `waves_per_simd` waves per SIMD on every CU.
+ * *flops receives the floating-point operations the launch performs (2·16·16·32 per MFMA).
+ * Errors: GEMM_ERR_INVALID (iters < 1, waves_per_simd not in 1..2, null flops), GEMM_ERR_HIP.
+ */
+gemm_status_t gemm_probe_mfma_peak(int64_t iters, int waves_per_simd, void* stream, double* flops);
+
+/*
+ * Launch a streaming copy of `bytes` (a multiple of 16) from src to dst with 16-byte loads and
+ * stores; used to read the HBM bandwidth and to scale memory-traffic counters.
+ * Errors: GEMM_ERR_INVALID (null pointer, bytes not a multiple of 16), GEMM_ERR_HIP.
+ */
+gemm_status_t gemm_probe_copy(const void* src, void* dst, int64_t bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPT_GEMM_H */

@@ -1,0 +1,85 @@
+// Internal definitions shared by the host plan code and the gfx950 kernels.
+//
+// The tile scheduler and the LDS swizzle are written once here as host+device functions, so
+// the host-only introspection entry points in gemm.h report exactly what the kernels do.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define SPT_HD __host__ __device__ __forceinline__
+
+namespace spt {
+
+constexpr int kNumXcd = 8;  // MI355X: 256 CUs in 8 XCDs; workgroups are dealt round-robin over XCDs
+
+// ---------------------------------------------------------------------------------------------
+// Tile scheduler ("GEMM II — pipelining with TMA", Step 6: a fixed pool of workgroups, each
+// walking many output tiles; l2_group_size groups tiles that share operands).
+//
+// 1. XCD remap: workgroup w runs on XCD w % 8. Logical worker ids are handed out so that the
+//    workgroups of one XCD hold a contiguous range of ids, hence a contiguous run of tiles in
+//    raster order, hence a compact block of the output that shares A rows and B rows in that
+//    XCD's L2.
+// 2. Round r of worker u processes tile t = r * grid + u (a static, precomputed assignment).
+// 3. Grouped raster: tiles are ordered in bands of group_m tile-rows; inside a band the order
+//    is column-major, so consecutive tiles share the same B column band and group_m A row bands.
+// ---------------------------------------------------------------------------------------------
+SPT_HD int xcd_remap(int w, int grid) {
+  const int x = w % kNumXcd, j = w / kNumXcd;
+  const int q = grid / kNumXcd, r = grid % kNumXcd;
+  return x * q + (x < r ? x : r) + j;
+}
+
+SPT_HD void grouped_raster(int t, int tiles_m, int tiles_n, int group_m, int& tm, int& tn) {
+  const int per_group = group_m * tiles_n;
+  const int g = t / per_group;
+  const int first_m = g * group_m;
+  const int rows_left = tiles_m - first_m;
+  const int gm = rows_left < group_m ? rows_left : group_m;
+  const int local = t - g * per_group;
+  tm = first_m + local % gm;
+  tn = local / gm;
+}
+
+// ---------------------------------------------------------------------------------------------
+// LDS operand layout ("Async Data Movement: TMA", How TMA Writes a Swizzled Layout and The
+// 128-Byte Swizzle Grouping Requirement). A tile of R rows x BK elements (16-bit) is stored as
+// BK/64 groups of [R rows x 128 bytes]; each 128-byte row is eight 16-byte chunks, and logical
+// chunk c of row r sits at physical chunk c XOR f(r).
+//
+// The pages use f(r) = r mod 8 (conflict-free for eight consecutive rows when 32 banks serve
+// eight 16-byte lanes per cycle). The MFMA operand reads here touch sixteen consecutive rows
+// at one chunk; f(r) = (r mod 8) XOR bit3(r) keeps those sixteen reads on sixteen distinct
+// 16-byte bank groups of a 64-bank LDS as well, while staying a bijection per row.
+// ---------------------------------------------------------------------------------------------
+SPT_HD int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+// byte offset of logical chunk c (0 .. BK/8-1) of row r in an R-row tile
+SPT_HD int lds_chunk_offset(int R, int r, int c) {
+  return (c >> 3) * (R * 128) + r * 128 + (((c & 7) ^ swz(r)) << 4);
+}
+
+// B rows are staged in a permuted order so that, after the MFMA (which hands each lane four
+// consecutive output columns per 16x16 block), a lane holds eight consecutive output columns
+// across the two blocks of a pair, enabling one 16-byte store. Within each 32-row group, LDS row
+// (h, g, i) = 16h + 4g + i holds global row 8g + 4h + i.
+SPT_HD int b_row_perm(int rho) {
+  const int base = rho & ~31, h = (rho >> 4) & 1, g = (rho >> 2) & 3, i = rho & 3;
+  return base + 8 * g + 4 * h + i;
+}
+
+// Kernel arguments (passed by value).
+struct GemmArgs {
+  const void* A;
+  const void* B;
+  void* C;
+  int M, N, K;
+  int lda, ldb, ldc;
+  int tiles_m, tiles_n, num_tiles;
+  int group_m;
+  int grid;
+  int out_dtype;  // 0 f16, 1 bf16, 2 f32
+};
+
+}  // namespace spt

@@ -1,0 +1,143 @@
+// Device-side helpers shared by the gfx950 GEMM kernels: vector types, wait-count and barrier
+// wrappers, buffer descriptors, the MFMA wrapper, the epilogue store and the tile geometry.
+#pragma once
+
+#include <type_traits>
+
+#include "spt_common.h"
+
+namespace spt {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+constexpr unsigned kOOB = 0x80000000u;       // voffset beyond every num_records: loads give 0, stores drop
+constexpr unsigned kMaxRecords = 0x7FFFFFF0u;
+constexpr int kRsrcWord3 = 0x00020000;       // raw buffer, 32-bit data format
+
+// ------------------------------------------------------------------------------ waits, barrier
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit counter");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
+
+// wait until at most t*LW of this wave's vector-memory operations are outstanding (t clamped to [0, T])
+template <int LW, int T>
+__device__ __forceinline__ void wait_vmcnt_tiles(int t) {
+  if constexpr (T <= 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (t >= T) wait_vmcnt<LW * T>();
+    else wait_vmcnt_tiles<LW, T - 1>(t);
+  }
+}
+
+__device__ __forceinline__ void barrier_sync() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint64_t bytes) {
+  const unsigned n = bytes > kMaxRecords ? kMaxRecords : (unsigned)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, kRsrcWord3);
+}
+
+// One direct global->LDS load: 64 lanes x 16 bytes from `r` at per-lane byte offset
+// voffset + soffset into the 1 KiB of LDS starting at `lds` (lane l lands at lds + 16*l).
+// Offsets at or beyond the descriptor's num_records read as zero.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, unsigned voffset, unsigned soffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, voffset, soffset, 0, 0);
+}
+
+// ------------------------------------------------------------------------------ MFMA
+template <typename TIn>
+__device__ __forceinline__ f32x4 mfma16(u32x4 x, u32x4 y, f32x4 c);
+template <>
+__device__ __forceinline__ f32x4 mfma16<__bf16>(u32x4 x, u32x4 y, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, x), __builtin_bit_cast(bf16x8, y), c,
+                                                 0, 0, 0);
+}
+template <>
+__device__ __forceinline__ f32x4 mfma16<_Float16>(u32x4 x, u32x4 y, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, x), __builtin_bit_cast(f16x8, y), c,
+                                                0, 0, 0);
+}
+
+// ------------------------------------------------------------------------------ epilogue
+__device__ __forceinline__ unsigned pack_bf16(float a, float b) {
+  return (unsigned)__builtin_bit_cast(unsigned short, (__bf16)a) |
+         ((unsigned)__builtin_bit_cast(unsigned short, (__bf16)b) << 16);
+}
+__device__ __forceinline__ unsigned pack_f16(float a, float b) {
+  return (unsigned)__builtin_bit_cast(unsigned short, (_Float16)a) |
+         ((unsigned)__builtin_bit_cast(unsigned short, (_Float16)b) << 16);
+}
+
+// Store the 8 consecutive outputs v[0..7] at row m_rel (relative to the tile's first row),
+// column n (absolute). OUT: 0 f16, 1 bf16, 2 f32. With EDGE, rows >= rows_left and columns
+// >= N are skipped element by element; without it the whole 8-wide segment is in range.
+template <int OUT, bool EDGE>
+__device__ __forceinline__ void store8(const float (&v)[8], __amdgpu_buffer_rsrc_t rc, int m_rel, int rows_left,
+                                      int n, int N, int ldc) {
+  if (EDGE && (m_rel >= rows_left || n >= N)) return;
+  if constexpr (OUT == 2) {
+    const unsigned off = (unsigned)(m_rel * ldc + n) * 4u;
+    if (!EDGE || n + 8 <= N) {
+      u32x4 lo = {__builtin_bit_cast(unsigned, v[0]), __builtin_bit_cast(unsigned, v[1]),
+                  __builtin_bit_cast(unsigned, v[2]), __builtin_bit_cast(unsigned, v[3])};
+      u32x4 hi = {__builtin_bit_cast(unsigned, v[4]), __builtin_bit_cast(unsigned, v[5]),
+                  __builtin_bit_cast(unsigned, v[6]), __builtin_bit_cast(unsigned, v[7])};
+      __builtin_amdgcn_raw_buffer_store_b128(lo, rc, off, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(hi, rc, off + 16u, 0, 0);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (n + e < N) __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v[e]), rc, off + 4u * e, 0, 0);
+    }
+  } else {
+    const unsigned off = (unsigned)(m_rel * ldc + n) * 2u;
+    unsigned p[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) p[e] = OUT == 1 ? pack_bf16(v[2 * e], v[2 * e + 1]) : pack_f16(v[2 * e], v[2 * e + 1]);
+    if (!EDGE || n + 8 <= N) {
+      u32x4 q = {p[0], p[1], p[2], p[3]};
+      __builtin_amdgcn_raw_buffer_store_b128(q, rc, off, 0, 0);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (n + e < N)
+          __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(p[e >> 1] >> (16 * (e & 1))), rc, off + 2u * e, 0, 0);
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------ the kernel
+template <int BM, int BN, int BK, int S, int WM, int WN>
+struct TileShape {
+  static constexpr int W = WM * WN, NT = 64 * W;
+  static constexpr int TM = BM / WM, TN = BN / WN;  // wave tile
+  static constexpr int FM = TM / 16, FN = TN / 16;  // 16-row fragments per wave (A side, B side)
+  static constexpr int NSUB = BK / 32;              // MFMA k-steps per K-tile
+  static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2, STAGE = A_BYTES + B_BYTES;
+  static constexpr int LDS = S * STAGE;
+  static constexpr int A_INSTR = A_BYTES / 1024, B_INSTR = B_BYTES / 1024;  // 1 KiB per DMA instruction
+  static constexpr int LA = A_INSTR / W, LB = B_INSTR / W, LW = LA + LB;   // per wave, per stage
+  static_assert(BK == 64 || BK == 128, "K-tile is one or two 128-byte swizzle groups");
+  static_assert(S >= 1 && S <= 4, "1..4 stages");
+  static_assert(TM % 16 == 0 && TN % 32 == 0, "wave tile: 16-row A fragments, pairs of 16-row B fragments");
+  static_assert(A_INSTR % W == 0 && B_INSTR % W == 0, "every wave issues the same number of loads");
+  static_assert(BM % 8 == 0 && BN % 32 == 0, "tile rows");
+  static_assert(LW * (S > 1 ? S - 1 : 1) < 64, "vmcnt thresholds fit the 6-bit counter");
+  static_assert(LDS <= 160 * 1024, "LDS ring fits the 160 KiB of a CU");
+  static_assert(NSUB % 2 == 0, "fragment double buffer parity");
+};
+
+}  // namespace spt

@@ -1,0 +1,70 @@
+// Measurement aids: a dense-MFMA throughput kernel (to confirm the peak the roofline divides by)
+// and a 16-byte streaming copy (HBM bandwidth, and the reference for scaling memory-traffic
+// counters). This translation unit is built with accumulators in VGPRs, which keeps the MFMA
+// chains in place without register copies.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "gemm.h"
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+#define SPT_MFMA(c) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0)
+
+__global__ void __launch_bounds__(256) mfma_peak_kernel(float* sink, int64_t iters) {
+  bf16x8 a, b;
+  for (int e = 0; e < 8; ++e) {
+    a[e] = (__bf16)(float)((threadIdx.x + e) % 3);
+    b[e] = (__bf16)(float)(e & 1);
+  }
+  f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = c0, c2 = c0, c3 = c0, c4 = c0, c5 = c0, c6 = c0, c7 = c0;
+  for (int64_t it = 0; it < iters; ++it) {
+    SPT_MFMA(c0); SPT_MFMA(c1); SPT_MFMA(c2); SPT_MFMA(c3); SPT_MFMA(c4); SPT_MFMA(c5); SPT_MFMA(c6); SPT_MFMA(c7);
+    SPT_MFMA(c0); SPT_MFMA(c1); SPT_MFMA(c2); SPT_MFMA(c3); SPT_MFMA(c4); SPT_MFMA(c5); SPT_MFMA(c6); SPT_MFMA(c7);
+  }
+  const f32x4 s = c0 + c1 + c2 + c3 + c4 + c5 + c6 + c7;
+  if (s[0] + s[1] + s[2] + s[3] == -1.0f) sink[0] = 1.0f;  // never true; keeps the chains alive
+}
+
+__global__ void __launch_bounds__(256) copy16_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst, int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) dst[i] = src[i];
+}
+
+float* g_sink[64] = {};
+
+}  // namespace
+
+extern "C" gemm_status_t gemm_probe_mfma_peak(int64_t iters, int waves_per_simd, void* stream, double* flops) {
+  if (iters < 1 || waves_per_simd < 1 || waves_per_simd > 2 || !flops) return GEMM_ERR_INVALID;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return GEMM_ERR_HIP;
+  if (!g_sink[dev] && hipMalloc(&g_sink[dev], sizeof(float)) != hipSuccess) return GEMM_ERR_HIP;
+  int cu = 0;
+  if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return GEMM_ERR_HIP;
+  const int grid = cu * waves_per_simd;  // 4 waves per workgroup: one per SIMD
+  hipLaunchKernelGGL(mfma_peak_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, g_sink[dev], iters);
+  if (hipGetLastError() != hipSuccess) return GEMM_ERR_HIP;
+  *flops = (double)grid * 4.0 * (double)iters * 16.0 * (2.0 * 16 * 16 * 32);
+  return GEMM_OK;
+}
+
+extern "C" gemm_status_t gemm_probe_copy(const void* src, void* dst, int64_t bytes, void* stream) {
+  if (!src || !dst || bytes < 0 || bytes % 16 != 0) return GEMM_ERR_INVALID;
+  if (bytes == 0) return GEMM_OK;
+  int dev = 0, cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return GEMM_ERR_HIP;
+  if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return GEMM_ERR_HIP;
+  const int64_t n = bytes / 16;
+  int64_t grid = (n + 255) / 256;
+  if (grid > (int64_t)cu * 16) grid = (int64_t)cu * 16;
+  hipLaunchKernelGGL(copy16_kernel, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, (const u32x4*)src,
+                     (u32x4*)dst, n);
+  if (hipGetLastError() != hipSuccess) return GEMM_ERR_HIP;
+  return GEMM_OK;
+}

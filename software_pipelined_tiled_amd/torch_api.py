@@ -1,0 +1,82 @@
+"""torch-tensor convenience over the C ABI: plans and a ``matmul`` that enqueues on torch's
+current stream. torch provides the device memory and the stream handle; all arithmetic runs in
+the HIP kernels.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+
+_DT = {torch.float16: _lib.GEMM_F16, torch.bfloat16: _lib.GEMM_BF16, torch.float32: _lib.GEMM_F32}
+
+
+def dtype_code(dt: torch.dtype) -> int:
+    if dt not in _DT:
+        raise TypeError(f"unsupported dtype {dt}")
+    return _DT[dt]
+
+
+class Plan:
+    """Owns a gemm_plan_t for C[M,N] = A[M,K]·B[N,K]ᵀ with the given dtypes and leading dimensions."""
+
+    def __init__(self, M, N, K, in_dtype: torch.dtype, out_dtype: torch.dtype, lda=None, ldb=None, ldc=None,
+                 config=None):
+        self.M, self.N, self.K = int(M), int(N), int(K)
+        self.lda = int(lda if lda is not None else K)
+        self.ldb = int(ldb if ldb is not None else K)
+        self.ldc = int(ldc if ldc is not None else N)
+        self.in_dtype, self.out_dtype = in_dtype, out_dtype
+        self.handle = None
+        self.handle = _lib.gemm_plan_create(self.M, self.N, self.K, dtype_code(in_dtype), dtype_code(in_dtype),
+                                            dtype_code(out_dtype), self.lda, self.ldb, self.ldc, config)
+
+    def describe(self) -> dict:
+        return _lib.gemm_plan_describe(self.handle)
+
+    def run_ptrs(self, a_ptr: int, b_ptr: int, c_ptr: int, stream: int | None = None) -> None:
+        if stream is None:
+            stream = torch.cuda.current_stream().cuda_stream
+        _lib.gemm_run(self.handle, a_ptr, b_ptr, c_ptr, stream)
+
+    def run(self, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, stream: int | None = None) -> torch.Tensor:
+        for name, t, rows, ld, dt in (("A", A, self.M, self.lda, self.in_dtype), ("B", B, self.N, self.ldb, self.in_dtype),
+                                      ("C", C, self.M, self.ldc, self.out_dtype)):
+            if not t.is_cuda or t.dtype != dt:
+                raise ValueError(f"{name} must be a {dt} device tensor")
+            if rows > 0 and (t.dim() != 2 or t.shape[0] < rows or t.stride(1) != 1 or t.stride(0) != ld):
+                raise ValueError(f"{name} must be [>= {rows}, *] row-major with stride {ld}")
+        self.run_ptrs(A.data_ptr(), B.data_ptr(), C.data_ptr(), stream)
+        return C
+
+    def close(self) -> None:
+        if self.handle is not None:
+            _lib.gemm_plan_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+_plan_cache: dict = {}
+
+
+def matmul(A: torch.Tensor, B: torch.Tensor, out_dtype: torch.dtype | None = None, out: torch.Tensor | None = None,
+           config: dict | None = None) -> torch.Tensor:
+    """C = A·Bᵀ for device tensors A[M,K], B[N,K] (row-major, unit column stride)."""
+    if A.dim() != 2 or B.dim() != 2 or A.shape[1] != B.shape[1]:
+        raise ValueError("A[M,K] and B[N,K] required")
+    M, K = A.shape
+    N = B.shape[0]
+    out_dtype = out_dtype or A.dtype
+    C = out if out is not None else torch.empty((M, N), dtype=out_dtype, device=A.device)
+    key = (M, N, K, A.dtype, out_dtype, A.stride(0), B.stride(0), C.stride(0),
+           tuple(sorted(config.items())) if config else None, A.device.index)
+    plan = _plan_cache.get(key)
+    if plan is None:
+        plan = Plan(M, N, K, A.dtype, out_dtype, A.stride(0), B.stride(0), C.stride(0), config)
+        _plan_cache[key] = plan
+    return plan.run(A, B, C)

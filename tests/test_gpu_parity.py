@@ -1,0 +1,176 @@
+"""GPU parity of the HIP GEMM against the CPU oracle, through the C ABI.
+
+* Small-integer operands (entries in [-3, 3], K·9 < 2^24) make every fp32 partial sum exact, so
+  every kernel configuration (tile, stage count, persistent or not, load path) must match the
+  oracle bit for bit: a race on a ring slot, a wrong swizzle or a dropped K-tile shows up as a
+  mismatch.
+* Real-valued operands (the workloads' distributions) are held to |C - C_ref| <= 2e-3·(|A|·|B|ᵀ)
+  + 1 ulp of the output type, elementwise.
+* Edge cases: ragged M/N/K, K below and around the stage depth, K = 0, padded leading
+  dimensions with NaN padding, misaligned base pointers (register-staged path), and that no
+  element outside [0, M) x [0, N) of C is written.
+* The full-size workloads run in the configuration the benchmark times and are checked on
+  sampled outputs (random positions plus every tile's corners).
+"""
+import numpy as np
+import pytest
+import torch
+
+import synthetic_inputs as si
+from oracle import oracle as orc
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # collected on CPU-only hosts, never run there
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import software_pipelined_tiled_amd as spt  # noqa: E402
+from gpu_helpers import check_full, check_sampled, run_gpu, sample_indices  # noqa: E402
+
+DMA_CONFIGS = [(256, 256, 2), (256, 256, 1), (256, 128, 3), (256, 128, 2), (256, 128, 1), (128, 128, 4),
+               (128, 128, 3), (128, 128, 2), (128, 128, 1), (64, 64, 4), (64, 64, 2)]
+REG_CONFIGS = [(128, 128, 2), (64, 64, 2)]
+
+
+def cfg(bm, bn, s, path=spt.GEMM_LOAD_DMA, persistent=1, group_m=8, grid=0):
+    return dict(bm=bm, bn=bn, bk=64, stages=s, waves=4, mfma=16, persistent=persistent, group_m=group_m,
+                load_path=path, grid=grid, lds_bytes=0)
+
+
+def ints(rows, cols, dtype, seed, ld=None):
+    return si.make_matrix(rows, cols, dtype, "small_int", seed, ld=ld)
+
+
+# ------------------------------------------------------------------------- bit-exact sweeps
+
+@pytest.mark.parametrize("bm,bn,s", DMA_CONFIGS)
+@pytest.mark.parametrize("persistent", [1, 0])
+def test_dma_configs_bit_exact(bm, bn, s, persistent):
+    # 3 x 2 tiles of (bm, bn) with ragged edges, K spanning several K-tiles plus a partial one
+    M, N, K = 2 * bm + bm // 2 + 3, 2 * bn - 5, 5 * 64 + 16
+    for in_dt in (si.F16, si.BF16):
+        a = ints(M, K, in_dt, 100 + bm + s)
+        b = ints(N, K, in_dt, 200 + bn + s)
+        # a small grid forces several rounds of the persistent loop
+        c, desc = run_gpu(a, b, K, in_dt, si.F32, config=cfg(bm, bn, s, persistent=persistent,
+                                                            grid=3 if persistent else 0))
+        assert desc["bm"] == bm and desc["stages"] == s and desc["load_path"] == spt.GEMM_LOAD_DMA
+        check_full(a, b, K, in_dt, si.F32, c, N, exact=True)
+
+
+@pytest.mark.parametrize("bm,bn,s", REG_CONFIGS)
+def test_reg_configs_bit_exact(bm, bn, s):
+    M, N, K = 2 * bm + 7, bn + 9, 3 * 64 + 13  # K not a multiple of 8: element-masked tail
+    for in_dt in (si.F16, si.BF16):
+        a = ints(M, K, in_dt, 300 + bm)
+        b = ints(N, K, in_dt, 400 + bn)
+        c, desc = run_gpu(a, b, K, in_dt, si.F32, config=cfg(bm, bn, s, path=spt.GEMM_LOAD_REG, grid=5))
+        assert desc["load_path"] == spt.GEMM_LOAD_REG
+        check_full(a, b, K, in_dt, si.F32, c, N, exact=True)
+
+
+@pytest.mark.parametrize("out_dt", [si.F16, si.BF16, si.F32])
+@pytest.mark.parametrize("in_dt", [si.F16, si.BF16])
+def test_output_dtypes_bit_exact(in_dt, out_dt):
+    # integer sums up to 9·K = 2880 are exact in every output type except bf16 (8 bits), where
+    # the oracle's single rounding of the exact sum must be reproduced exactly as well
+    M, N, K = 300, 264, 320
+    a = ints(M, K, in_dt, 7)
+    b = ints(N, K, in_dt, 8)
+    for c_cfg in (cfg(256, 256, 2), cfg(128, 128, 4), cfg(128, 128, 2, path=spt.GEMM_LOAD_REG)):
+        c, _ = run_gpu(a, b, K, in_dt, out_dt, config=c_cfg)
+        check_full(a, b, K, in_dt, out_dt, c, N, exact=True)
+
+
+@pytest.mark.parametrize("K", [1, 8, 63, 64, 65, 127, 128, 129, 200, 256])
+@pytest.mark.parametrize("s", [1, 2, 3, 4])
+def test_k_around_stage_depth(K, s):
+    # fewer K-tiles than stages, exactly S, and S + 1: prologue, drain and the masked K tail
+    M, N = 130, 96
+    a = ints(M, K, si.BF16, K)
+    b = ints(N, K, si.BF16, K + 1)
+    conf = cfg(128, 128, s) if K % 8 == 0 else cfg(128, 128, 2, path=spt.GEMM_LOAD_REG)
+    c, _ = run_gpu(a, b, K, si.BF16, si.F32, config=conf)
+    check_full(a, b, K, si.BF16, si.F32, c, N, exact=True)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 1), (17, 33, 65), (255, 257, 63), (256, 256, 256), (8, 8, 8),
+                                   (300, 200, 72), (1, 300, 64), (300, 1, 64), (64, 64, 4096)])
+def test_edge_shapes_auto_config(M, N, K):
+    for in_dt in (si.F16, si.BF16):
+        a = ints(M, K, in_dt, M + 3 * N)
+        b = ints(N, K, in_dt, N + 5 * K)
+        c, _ = run_gpu(a, b, K, in_dt, si.F32)
+        check_full(a, b, K, in_dt, si.F32, c, N, exact=True)
+
+
+def test_k_zero_writes_zeros():
+    for conf in (None, cfg(64, 64, 2, path=spt.GEMM_LOAD_REG)):
+        a = np.zeros((70, 8), np.uint16)
+        b = np.zeros((40, 8), np.uint16)
+        c, _ = run_gpu(a, b, 0, si.F16, si.F16, config=conf)
+        assert np.all(c[:, :40] == 0)
+
+
+def test_padded_ld_and_no_out_of_bounds_writes():
+    M, N, K = 200, 136, 192
+    for in_dt in (si.F16, si.BF16):
+        # NaN in the A/B padding: reading it would poison the sums
+        a = si.make_matrix(M, K, in_dt, "small_int", 21, ld=K + 64, pad_bits=0x7E00 if in_dt == si.F16 else 0x7FC0)
+        b = si.make_matrix(N, K, in_dt, "small_int", 22, ld=K + 8, pad_bits=0x7E00 if in_dt == si.F16 else 0x7FC0)
+        for out_dt in (si.F16, si.F32):
+            ldc = N + 24
+            c, desc = run_gpu(a, b, K, in_dt, out_dt, ldc=ldc)
+            assert desc["load_path"] == spt.GEMM_LOAD_DMA
+            check_full(a, b, K, in_dt, out_dt, c, N, exact=True)
+            pad = orc.decode(out_dt, c[:, N:])
+            assert np.all(np.isnan(pad)), "the ldc padding of C was written"
+
+
+def test_misaligned_pointers_use_register_path():
+    M, N, K = 150, 120, 128
+    a = ints(M, K, si.F16, 31)
+    b = ints(N, K, si.F16, 32)
+    c, desc = run_gpu(a, b, K, si.F16, si.F32, a_off=1, b_off=3)
+    check_full(a, b, K, si.F16, si.F32, c, N, exact=True)
+
+
+def test_deterministic_and_grouping_invariant():
+    M, N, K = 520, 700, 448
+    a = si.make_matrix(M, K, si.BF16, "normal_scaled", 41, k_for_scale=K)
+    b = si.make_matrix(N, K, si.BF16, "normal_scaled", 42, k_for_scale=K)
+    c1, _ = run_gpu(a, b, K, si.BF16, si.BF16, config=cfg(128, 128, 4, group_m=8))
+    c2, _ = run_gpu(a, b, K, si.BF16, si.BF16, config=cfg(128, 128, 4, group_m=8))
+    c3, _ = run_gpu(a, b, K, si.BF16, si.BF16, config=cfg(128, 128, 4, group_m=1, persistent=0))
+    assert np.array_equal(c1, c2) and np.array_equal(c1, c3)  # tile order does not change any sum
+    check_full(a, b, K, si.BF16, si.BF16, c1, N)
+
+
+# ------------------------------------------------------------------------- the workloads
+
+def test_c1_256_f16_to_f32_full():
+    m, n, k, a, b, i_dt, o_dt = si.workload_operands("c1_256_f16_f32")
+    c, _ = run_gpu(a, b, k, i_dt, o_dt)
+    rep = check_full(a, b, k, i_dt, o_dt, c, n)
+    print("c1 max |err|/tol", rep["max_ratio"], flush=True)
+
+
+@pytest.mark.parametrize("name,shape_index", [("c2_4096_f16_f16", 0), ("c3_8192_bf16_bf16", 0),
+                                              ("c4_16384x16384x1024_bf16", 0), ("c5_skinny_ragged_f16", 0),
+                                              ("c5_skinny_ragged_f16", 1), ("c5_skinny_ragged_f16", 2)])
+def test_workload_sampled(name, shape_index):
+    m, n, k, a, b, i_dt, o_dt = si.workload_operands(name, shape_index)
+    print(f"{name}[{shape_index}] M={m} N={n} K={k}", flush=True)
+    c, desc = run_gpu(a, b, k, i_dt, o_dt, c_sentinel=True)
+    ii, jj = sample_indices(m, n, desc["bm"], desc["bn"], 2048, seed=m + n + k)
+    rep = check_sampled(a, b, k, i_dt, o_dt, c, ii, jj)
+    print(f"  config {desc}  samples {rep['n']}  max |err|/tol {rep['max_ratio']:.3g}", flush=True)
+    # every output was written and is finite
+    assert np.all(np.isfinite(orc.decode(o_dt, c[:, :n]) if o_dt != si.F32 else c[:, :n]))
+
+
+def test_workload_c1_small_full_through_each_dma_config():
+    m, n, k, a, b, i_dt, o_dt = si.workload_operands("c1_256_f16_f32")
+    for bm, bn, s in DMA_CONFIGS:
+        c, _ = run_gpu(a, b, k, i_dt, o_dt, config=cfg(bm, bn, s))
+        check_full(a, b, k, i_dt, o_dt, c, n)
