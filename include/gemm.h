@@ -164,6 +164,16 @@ gemm_status_t gemm_probe_mfma_peak(int64_t iters, int waves_per_simd, void* stre
  */
 gemm_status_t gemm_probe_copy(const void* src, void* dst, int64_t bytes, void* stream);
 
+/*
+ * Launch an LDS read-pattern kernel (one workgroup of 4 waves per CU, `iters` x 8 ds_read_b128
+ * per lane). swizzle -1: lane l reads 16*l (the conflict-free reference); 0..4: lane l reads row
+ * l%16, 16-byte chunk l/16 of a 128-byte-row tile, with the physical chunk XOR-ed by
+ * 0: nothing, 1: row%8, 2: (row%8) XOR bit3(row), 3: (row/2)%8, 4: (row%4) XOR (bit2(row)<<2).
+ * Read with the SQ_LDS_BANK_CONFLICT counter to compare LDS layouts.
+ * Errors: GEMM_ERR_INVALID (swizzle outside -1..4, iters < 1), GEMM_ERR_HIP.
+ */
+gemm_status_t gemm_probe_lds_read(int swizzle, int64_t iters, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -19,7 +19,7 @@ GEMM_LOAD_AUTO, GEMM_LOAD_DMA, GEMM_LOAD_REG = 0, 1, 2
 # every entry point include/gemm.h declares
 EXPORTS = ("gemm_plan_create", "gemm_run", "gemm_plan_destroy", "gemm_plan_describe", "gemm_status_string",
            "gemm_select_config", "gemm_schedule_tile", "gemm_lds_chunk_offset", "gemm_probe_mfma_peak",
-           "gemm_probe_copy")
+           "gemm_probe_copy", "gemm_probe_lds_read")
 
 
 class GemmLibraryMissing(ImportError):
@@ -80,6 +80,8 @@ def lib() -> ctypes.CDLL:
     L.gemm_probe_mfma_peak.argtypes = [i64, i32, vp, P(ctypes.c_double)]
     L.gemm_probe_copy.restype = i32
     L.gemm_probe_copy.argtypes = [vp, vp, i64, vp]
+    L.gemm_probe_lds_read.restype = i32
+    L.gemm_probe_lds_read.argtypes = [i32, i64, vp]
     _lib = L
     return L
 
@@ -155,3 +157,7 @@ def gemm_probe_mfma_peak(iters: int, waves_per_simd: int = 2, stream: int = 0) -
 
 def gemm_probe_copy(src_ptr: int, dst_ptr: int, nbytes: int, stream: int = 0) -> None:
     _check(lib().gemm_probe_copy(src_ptr, dst_ptr, nbytes, stream or None), "gemm_probe_copy")
+
+
+def gemm_probe_lds_read(swizzle: int, iters: int, stream: int = 0) -> None:
+    _check(lib().gemm_probe_lds_read(swizzle, iters, stream or None), "gemm_probe_lds_read")

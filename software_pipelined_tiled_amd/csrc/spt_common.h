@@ -48,12 +48,10 @@ SPT_HD void grouped_raster(int t, int tiles_m, int tiles_n, int group_m, int& tm
 // BK/64 groups of [R rows x 128 bytes]; each 128-byte row is eight 16-byte chunks, and logical
 // chunk c of row r sits at physical chunk c XOR f(r).
 //
-// The pages use f(r) = r mod 8 (conflict-free for eight consecutive rows when 32 banks serve
-// eight 16-byte lanes per cycle). The MFMA operand reads here touch sixteen consecutive rows
-// at one chunk; f(r) = (r mod 8) XOR bit3(r) keeps those sixteen reads on sixteen distinct
-// 16-byte bank groups of a 64-bank LDS as well, while staying a bijection per row.
-// ---------------------------------------------------------------------------------------------
-SPT_HD int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+// f(r) = r mod 8, the pages' 128-byte swizzle. Measured on gfx950 with SQ_LDS_BANK_CONFLICT
+// for the MFMA operand read (16 consecutive rows at one chunk per 64-lane ds_read_b128), it is
+// conflict-free, where the unswizzled layout is 4-way conflicted.
+SPT_HD int swz(int r) { return r & 7; }
 
 // byte offset of logical chunk c (0 .. BK/8-1) of row r in an R-row tile
 SPT_HD int lds_chunk_offset(int R, int r, int c) {

@@ -3,6 +3,7 @@
 #pragma once
 
 #include <type_traits>
+#include <utility>
 
 #include "spt_common.h"
 
@@ -55,6 +56,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // Offsets at or beyond the descriptor's num_records read as zero.
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, unsigned voffset, unsigned soffset) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, voffset, soffset, 0, 0);
+}
+
+// static_for<N>(f): f(std::integral_constant<int, 0>{}) ... f(std::integral_constant<int, N-1>{}),
+// so loop indices that select code paths are compile-time constants.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 // ------------------------------------------------------------------------------ MFMA

@@ -37,18 +37,19 @@ __global__ void __launch_bounds__(WM* WN * 64, 1) gemm_dma_kernel(GemmArgs args)
 
   // DMA address map. A instruction j of this wave fills LDS bytes [(wave*LA + j) * 1024, +1024)
   // of the stage's A region: rows rho = 8*rb + lane/8 of 64-wide group g; the lane's physical
-  // chunk lane%8 must hold logical chunk c = (lane%8) XOR swz(rho), so it fetches that chunk.
-  auto a_map = [&](int j, int& row, int& kc) {
-    const int q = wave * T::LA + j, g = q / (BM / 8), rb = q % (BM / 8);
-    const int rho = 8 * rb + (lane >> 3);
-    row = rho;
-    kc = 8 * (8 * g + ((lane & 7) ^ swz(rho)));
+  // chunk lane%8 must hold logical chunk (lane%8) XOR swz(rho). The swizzle has period 8 in the
+  // row, so swz(rho) = swz(lane/8) and the chunk depends on the lane alone; the group g is
+  // wave-uniform. Element offset of the lane's chunk inside the K-tile: 64*g + lane_kc.
+  const int lane_kc = 8 * ((lane & 7) ^ swz(lane >> 3));
+  auto a_map = [&](int j, int& row, int& g) {
+    const int q = wave * T::LA + j, rb = q % (BM / 8);
+    g = q / (BM / 8);
+    row = 8 * rb + (lane >> 3);
   };
-  auto b_map = [&](int j, int& row, int& kc) {
-    const int q = wave * T::LB + j, g = q / (BN / 8), rb = q % (BN / 8);
-    const int rho = 8 * rb + (lane >> 3);
-    row = b_row_perm(rho);
-    kc = 8 * (8 * g + ((lane & 7) ^ swz(rho)));
+  auto b_map = [&](int j, int& row, int& g) {
+    const int q = wave * T::LB + j, rb = q % (BN / 8);
+    g = q / (BN / 8);
+    row = b_row_perm(8 * rb + (lane >> 3));
   };
   // fragment read offsets for k-step `sub` at f = 0 (fragment f adds 16 rows = 2048 bytes)
   int a_rd[T::NSUB], b_rd[T::NSUB];
@@ -66,58 +67,56 @@ __global__ void __launch_bounds__(WM* WN * 64, 1) gemm_dma_kernel(GemmArgs args)
     const int row0 = tm * BM, col0 = tn * BN;
     const int rows_left = M - row0, cols_left = N - col0;
     const bool full_tile = rows_left >= BM && cols_left >= BN;
-
     const __amdgpu_buffer_rsrc_t ra =
         make_rsrc((const char*)args.A + (size_t)row0 * args.lda * 2, ((uint64_t)(rows_left - 1) * args.lda + K) * 2);
     const __amdgpu_buffer_rsrc_t rb =
         make_rsrc((const char*)args.B + (size_t)col0 * args.ldb * 2, ((uint64_t)(cols_left - 1) * args.ldb + K) * 2);
 
-    // byte offset of each lane's chunk at k = 0, or kOOB for rows past the matrix edge
+    // byte offset of each lane's chunk at k = 0; rows past the matrix edge get an offset beyond
+    // num_records (it stays beyond it after adding 2*k0 < 2^31), so they read zeros
     unsigned a_off[T::LA], b_off[T::LB];
 #pragma unroll
     for (int j = 0; j < T::LA; ++j) {
-      int row, kc;
-      a_map(j, row, kc);
-      a_off[j] = row < rows_left ? (unsigned)(row * args.lda + kc) * 2u : kOOB;
+      int row, g;
+      a_map(j, row, g);
+      a_off[j] = row < rows_left ? (unsigned)(row * args.lda + 64 * g + lane_kc) * 2u : kOOB;
     }
 #pragma unroll
     for (int j = 0; j < T::LB; ++j) {
-      int row, kc;
-      b_map(j, row, kc);
-      b_off[j] = row < cols_left ? (unsigned)(row * args.ldb + kc) * 2u : kOOB;
+      int row, g;
+      b_map(j, row, g);
+      b_off[j] = row < cols_left ? (unsigned)(row * args.ldb + 64 * g + lane_kc) * 2u : kOOB;
     }
 
-    // issue this wave's share of K-tile kt into ring slot `slot`
-    auto issue = [&](int slot, int kt) {
+    // DMA instruction d (0 .. LW-1: A loads first, then B) of this wave's share of K-tile kt,
+    // into ring slot `slot`. Branch-free: a chunk at or past K (lane_kc >= K - k0 - 64*g, a scalar
+    // bound) reads zeros, so K-tiles past the end are zero-filling dummies; every hand-over issues
+    // exactly LW loads per wave, which keeps every vmcnt threshold constant.
+    auto dma_one = [&](int slot, int kt, int d) {
       const int k0 = kt * BK;
-      char* sa = smem + slot * T::STAGE + wave * T::LA * 1024;
-      char* sb = smem + slot * T::STAGE + T::A_BYTES + wave * T::LB * 1024;
-      if (full_tile && k0 + BK <= K) {  // interior: every chunk valid, the k offset rides in soffset
-#pragma unroll
-        for (int j = 0; j < T::LA; ++j)
-          dma16(ra, sa + j * 1024, a_off[j], 2u * k0);
-#pragma unroll
-        for (int j = 0; j < T::LB; ++j)
-          dma16(rb, sb + j * 1024, b_off[j], 2u * k0);
-      } else {  // edge tile or K tail: chunks past K or past the last row read zeros
-#pragma unroll
-        for (int j = 0; j < T::LA; ++j) {
-          int row, kc;
-          a_map(j, row, kc);
-          const unsigned vo = (k0 + kc < K && a_off[j] != kOOB) ? a_off[j] + 2u * k0 : kOOB;
-          dma16(ra, sa + j * 1024, vo, 0u);
-        }
-#pragma unroll
-        for (int j = 0; j < T::LB; ++j) {
-          int row, kc;
-          b_map(j, row, kc);
-          const unsigned vo = (k0 + kc < K && b_off[j] != kOOB) ? b_off[j] + 2u * k0 : kOOB;
-          dma16(rb, sb + j * 1024, vo, 0u);
-        }
+      if (d < T::LA) {
+        const int g = (wave * T::LA + d) / (BM / 8);
+        char* sa = smem + slot * T::STAGE + (wave * T::LA + d) * 1024;
+        dma16(ra, sa, lane_kc < K - k0 - 64 * g ? a_off[d] + 2u * k0 : kOOB, 0u);
+      } else {
+        const int j = d - T::LA;
+        const int g = (wave * T::LB + j) / (BN / 8);
+        char* sb = smem + slot * T::STAGE + T::A_BYTES + (wave * T::LB + j) * 1024;
+        dma16(rb, sb, lane_kc < K - k0 - 64 * g ? b_off[j] + 2u * k0 : kOOB, 0u);
       }
+    };
+    auto issue = [&](int slot, int kt) {
+#pragma unroll
+      for (int d = 0; d < T::LW; ++d) dma_one(slot, kt, d);
     };
 
     u32x4 xf[2][T::FN], yf[2][T::FM];  // fragment double buffer: B side (x), A side (y)
+    // fragment r of k-step `sub` (r < FN: B side, else A side) into buffer `buf`
+    auto read_frag = [&](int slot, int sub, int buf, int r) {
+      const char* base = smem + slot * T::STAGE;
+      if (r < T::FN) xf[buf][r] = *(const u32x4*)(base + b_rd[sub] + r * 2048);
+      else yf[buf][r - T::FN] = *(const u32x4*)(base + a_rd[sub] + (r - T::FN) * 2048);
+    };
     auto read_frags = [&](int slot, int sub, int buf) {
       const char* base = smem + slot * T::STAGE;
 #pragma unroll
@@ -132,39 +131,79 @@ __global__ void __launch_bounds__(WM* WN * 64, 1) gemm_dma_kernel(GemmArgs args)
     f32x4 acc[T::FN][T::FM];
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
-    // one K-tile: k-steps 0 .. NSUB-1 of `slot`; the last k-step hands over to tile k+1
-    auto k_tile = [&](int k, int slot, auto first_tile_c) {
-      constexpr bool kFirst = decltype(first_tile_c)::value;
+    // One k-step: the FN x FM MFMAs on fragment buffer `buf`, with NR fragment reads (for the next
+    // k-step) and ND DMA loads (for a later K-tile) threaded between them, one per MFMA slot, the
+    // reads first. The order is pinned (sched_barrier) so the loads drain through the
+    // vector-memory and LDS pipes while the MFMA pipe stays busy, instead of arriving in a burst.
+    constexpr int NM = T::FN * T::FM;
+    auto kstep = [&](int buf, auto zero_c, auto nr_c, auto nd_c, auto&& rd, auto&& dm) {
+      constexpr bool kZero = decltype(zero_c)::value;
+      constexpr int NR = decltype(nr_c)::value, ND = decltype(nd_c)::value;
+      static_assert(NR + ND <= 2 * NM, "at most two loads per MFMA slot");
+      static_for<NM>([&](auto m_c) {
+        constexpr int m = decltype(m_c)::value;
+        constexpr int i = m / T::FM, j = m % T::FM;
+        acc[i][j] = mfma16<TIn>(xf[buf][i], yf[buf][j], kZero ? zero4 : acc[i][j]);
+        // load slots: reads take slots 0 .. NR-1, DMAs the following ND (two per MFMA if needed)
+        constexpr int per = (NR + ND + NM - 1) / NM;
+        static_for<per>([&](auto q_c) {
+          constexpr int L = m * per + decltype(q_c)::value;
+          if constexpr (L < NR) rd(L);
+          else if constexpr (L < NR + ND) dm(L - NR);
+        });
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    };
+    auto no_load = [](int) {};
+
+    // One K-tile: k-steps 0 .. NSUB-1 of ring slot `slot`. Before the last k-step of every tile
+    // but the last (kHandover, a compile-time flag so that the K-loop body is one straight-line
+    // block whose accumulators never meet at a join): wait for tile k+1, sync, then (threaded through the MFMAs) read tile k+1's
+    // first fragments and refill `slot` with tile k+S. The refill is split in two halves so the
+    // loads spread over a whole K-tile: the first half in this hand-over k-step, the second half
+    // in k-step 0 of the next tile (kDefer). The slot stays free from this hand-over's barrier to
+    // the next one, and by the next hand-over every load of tile k+S has been issued, so the
+    // vmcnt thresholds are unchanged. kFirst: the first tile, whose MFMA chains start from zero.
+    constexpr int LW1 = S > 1 ? T::LW / 2 : 0;  // refill loads issued in the hand-over k-step
+    auto k_tile = [&](int k, int slot, auto first_c, auto handover_c) {
+      constexpr bool kFirst = decltype(first_c)::value;
+      constexpr bool kHandover = decltype(handover_c)::value;
+      constexpr bool kDefer = !kFirst && S > 1;
       const int next_slot = slot + 1 == S ? 0 : slot + 1;
-#pragma unroll
-      for (int sub = 0; sub < T::NSUB; ++sub) {
-        const int buf = sub & 1;
-        if (sub + 1 < T::NSUB) {
-          read_frags(slot, sub + 1, buf ^ 1);
-        } else if (k + 1 < KT) {
+      const int prev_slot = slot == 0 ? S - 1 : slot - 1;
+      static_for<T::NSUB>([&](auto sub_c) {
+        constexpr int sub = decltype(sub_c)::value;
+        constexpr int buf = sub & 1;
+        auto zero_c = std::integral_constant<bool, kFirst && (sub == 0)>{};
+        auto nr_c = std::integral_constant<int, T::FN + T::FM>{};
+        // second half of the refill started at the previous hand-over: tile k-1+S into prev_slot
+        auto nd_def = std::integral_constant<int, (kDefer && sub == 0) ? T::LW - LW1 : 0>{};
+        auto dm_def = [&](int d) { dma_one(prev_slot, k - 1 + S, LW1 + d); };
+        if constexpr (sub + 1 < T::NSUB) {
+          kstep(buf, zero_c, nr_c, nd_def, [&](int r) { read_frag(slot, sub + 1, buf ^ 1, r); }, dm_def);
+        } else if constexpr (kHandover) {
           wait_lgkmcnt0();  // this wave's reads of `slot` are done
           if constexpr (S == 1) {
             // serial: the only slot is refilled once everyone has read it, then waited on
             barrier_sync();
             issue(0, k + 1);
             wait_vmcnt<0>();
+            barrier_sync();
+            kstep(buf, zero_c, nr_c, std::integral_constant<int, 0>{},
+                  [&](int r) { read_frag(0, 0, buf ^ 1, r); }, no_load);
           } else {
-            // tiles issued so far: 0 .. min(k+S-1, KT-1); tile k+1 must have landed
-            const int ahead = (k + S - 1 < KT - 1 ? k + S - 1 : KT - 1) - (k + 1);
-            if (ahead >= S - 2) wait_vmcnt<T::LW * (S - 2)>();
-            else wait_vmcnt_tiles<T::LW, (S > 2 ? S - 3 : 0)>(ahead);
+            // every hand-over issued LW loads, so exactly tiles k+2 .. k+S-1 may still be in flight
+            wait_vmcnt<T::LW * (S - 2)>();
+            barrier_sync();  // tile k+1 visible to all waves; `slot` free in all waves
+            static_assert(T::NSUB >= 2, "the deferred half needs a k-step before the hand-over");
+            kstep(buf, zero_c, nr_c, std::integral_constant<int, LW1>{},
+                  [&](int r) { read_frag(next_slot, 0, buf ^ 1, r); },
+                  [&](int d) { dma_one(slot, k + S, d); });
           }
-          barrier_sync();  // tile k+1 visible to all waves; `slot` free in all waves
-          if constexpr (S > 1)
-            if (k + S < KT) issue(slot, k + S);
-          read_frags(next_slot, 0, buf ^ 1);
+        } else {
+          kstep(buf, zero_c, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, no_load, no_load);
         }
-#pragma unroll
-        for (int i = 0; i < T::FN; ++i)
-#pragma unroll
-          for (int j = 0; j < T::FM; ++j)
-            acc[i][j] = mfma16<TIn>(xf[buf][i], yf[buf][j], (kFirst && sub == 0) ? zero4 : acc[i][j]);
-      }
+      });
     };
 
     const int es = OUT == 2 ? 4 : 2;
@@ -188,18 +227,24 @@ __global__ void __launch_bounds__(WM* WN * 64, 1) gemm_dma_kernel(GemmArgs args)
     first_tile = false;
     // ---- prologue: fill the ring with tiles 0 .. min(S, KT) - 1 ----
 #pragma unroll
-    for (int s = 0; s < S; ++s)
-      if (s < KT) issue(s, s);
-    wait_vmcnt_tiles<T::LW, S - 1>((KT < S ? KT : S) - 1);  // this wave's part of tile 0 landed
-    barrier_sync();                                          // ... and every wave's
+    for (int s = 0; s < S; ++s) issue(s, s);  // tiles past K are zero-filling dummies
+    wait_vmcnt<T::LW * (S - 1)>();            // this wave's part of tile 0 landed
+    barrier_sync();                           // ... and every wave's
     read_frags(0, 0, 0);
 
-    // ---- steady state and drain: one barrier per K-tile ----
-    k_tile(0, 0, std::true_type{});
-    int slot = S > 1 ? 1 : 0;
-    for (int k = 1; k < KT; ++k) {
-      k_tile(k, slot, std::false_type{});
-      slot = slot + 1 == S ? 0 : slot + 1;
+    // ---- steady state and drain: one barrier per K-tile; the last K-tile is peeled ----
+    using t_ = std::true_type;
+    using f_ = std::false_type;
+    if (KT == 1) {
+      k_tile(0, 0, t_{}, f_{});
+    } else {
+      k_tile(0, 0, t_{}, t_{});
+      int slot = S > 1 ? 1 : 0;
+      for (int k = 1; k < KT - 1; ++k) {
+        k_tile(k, slot, f_{}, t_{});
+        slot = slot + 1 == S ? 0 : slot + 1;
+      }
+      k_tile(KT - 1, slot, f_{}, f_{});
     }
 
     // ---- epilogue: fp32 -> output type, 8 consecutive columns per lane ----
@@ -218,6 +263,7 @@ __global__ void __launch_bounds__(WM* WN * 64, 1) gemm_dma_kernel(GemmArgs args)
           const int m_rel = wm * T::TM + 16 * j + (lane & 15);
           const int n = col0 + wn * T::TN + 32 * pu + 8 * (lane >> 4);
           store8<OUT, kEdge>(v, rc, m_rel, rows_left, n, N, args.ldc);
+          __builtin_amdgcn_sched_barrier(0);  // one 8-value chunk of accumulators live at a time
         }
       }
     };
@@ -244,6 +290,9 @@ static KernelEntry make_entry() {
 
 const KernelEntry* dma_kernel_table(int* count) {
   static const KernelEntry table[] = {
+      make_entry<256, 256, 64, 2, 2, 4>(),
+      make_entry<256, 256, 64, 2, 4, 2>(),
+      make_entry<256, 256, 64, 1, 2, 4>(),
       make_entry<256, 256, 64, 2, 2, 2>(),
       make_entry<256, 256, 64, 1, 2, 2>(),
       make_entry<256, 128, 64, 3, 2, 2>(),

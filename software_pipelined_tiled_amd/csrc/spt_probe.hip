@@ -36,6 +36,34 @@ __global__ void __launch_bounds__(256) copy16_kernel(const u32x4* __restrict__ s
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) dst[i] = src[i];
 }
 
+// LDS read-pattern probe: every lane issues ds_read_b128 at the MFMA operand-read address
+// (row lane%16, 16-byte chunk lane/16 of a 128-byte-row tile) under swizzle `sw`, or at 16*lane
+// for sw < 0. Used with SQ_LDS_BANK_CONFLICT to choose the LDS layout.
+__device__ __forceinline__ int probe_swizzle(int sw, int r) {
+  switch (sw) {
+    case 0: return 0;
+    case 1: return r & 7;
+    case 2: return (r & 7) ^ ((r >> 3) & 1);
+    case 3: return (r >> 1) & 7;
+    default: return (r & 3) ^ (((r >> 2) & 1) << 2);
+  }
+}
+
+__global__ void __launch_bounds__(256) lds_read_kernel(unsigned* sink, int sw, int64_t iters) {
+  __shared__ __attribute__((aligned(1024))) char smem[32768];
+  for (int i = threadIdx.x; i < 32768 / 4; i += 256) ((unsigned*)smem)[i] = (unsigned)i * 2654435761u;
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, c = lane >> 4;
+  const int addr = sw < 0 ? wave * 1024 + 16 * lane : (wave * 16 + r) * 128 + ((c ^ probe_swizzle(sw, r)) & 7) * 16;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc ^= *(volatile u32x4*)(smem + ((addr + j * 8192) & 32767));
+  }
+  if ((acc[0] ^ acc[1] ^ acc[2] ^ acc[3]) == 0x12345678u) sink[0] = 1u;  // keeps the reads alive
+}
+
 float* g_sink[64] = {};
 
 }  // namespace
@@ -65,6 +93,18 @@ extern "C" gemm_status_t gemm_probe_copy(const void* src, void* dst, int64_t byt
   if (grid > (int64_t)cu * 16) grid = (int64_t)cu * 16;
   hipLaunchKernelGGL(copy16_kernel, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, (const u32x4*)src,
                      (u32x4*)dst, n);
+  if (hipGetLastError() != hipSuccess) return GEMM_ERR_HIP;
+  return GEMM_OK;
+}
+
+extern "C" gemm_status_t gemm_probe_lds_read(int swizzle, int64_t iters, void* stream) {
+  if (swizzle < -1 || swizzle > 4 || iters < 1) return GEMM_ERR_INVALID;
+  int dev = 0, cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return GEMM_ERR_HIP;
+  if (!g_sink[dev] && hipMalloc(&g_sink[dev], sizeof(float)) != hipSuccess) return GEMM_ERR_HIP;
+  if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return GEMM_ERR_HIP;
+  hipLaunchKernelGGL(lds_read_kernel, dim3(cu), dim3(256), 0, (hipStream_t)stream, (unsigned*)g_sink[dev], swizzle,
+                     iters);
   if (hipGetLastError() != hipSuccess) return GEMM_ERR_HIP;
   return GEMM_OK;
 }

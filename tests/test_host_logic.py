@@ -188,14 +188,14 @@ def test_lds_page_bank_example():
         assert len(sectors) == g["ungrouped_distinct"]
 
 
-def test_lds_mfma_read_pattern_conflict_free():
-    # one MFMA operand read: 16 consecutive rows at one chunk; 64 banks x 4 bytes = 16 bank groups
-    # of 16 bytes. All 16 reads must land on distinct groups, for every chunk and 16-row block.
+def test_lds_swizzle_spreads_every_eight_row_column():
+    # the property the pages state for the 128-byte swizzle: the same logical 16-byte chunk of
+    # eight consecutive rows sits in eight different physical chunk positions (bank sectors)
     for bk in (64, 128):
-        for base in range(0, 256, 16):
+        for base in range(0, 256, 8):
             for c in range(bk // 8):
-                groups = {(spt.gemm_lds_chunk_offset(256, bk, base + i, c) // 16) % 16 for i in range(16)}
-                assert len(groups) == 16
+                pos = {(spt.gemm_lds_chunk_offset(256, bk, base + i, c) % 128) // 16 for i in range(8)}
+                assert len(pos) == 8
 
 
 # ------------------------------------------------------------------------------ stage bytes
