@@ -89,20 +89,22 @@ __global__ void __launch_bounds__(WM* WN * 64, 1) gemm_dma_kernel(GemmArgs args)
     }
 
     // DMA instruction d (0 .. LW-1: A loads first, then B) of this wave's share of K-tile kt,
-    // into ring slot `slot`. Branch-free: a chunk at or past K (lane_kc >= K - k0 - 64*g, a scalar
-    // bound) reads zeros, so K-tiles past the end are zero-filling dummies; every hand-over issues
-    // exactly LW loads per wave, which keeps every vmcnt threshold constant.
+    // into ring slot `slot`. The K offset rides in the scalar soffset; the per-lane voffset is a
+    // constant, replaced by one past num_records (reads zero) when the lane's chunk lies at or past
+    // K (lane_kc >= K - k0 - 64*g: one compare per group and K-tile). K-tiles past the end are
+    // therefore zero-filling dummies, and every hand-over issues exactly LW loads per wave, which
+    // keeps every vmcnt threshold constant. (kOOB + soffset stays past num_records: soffset < 2^31.)
     auto dma_one = [&](int slot, int kt, int d) {
       const int k0 = kt * BK;
       if (d < T::LA) {
         const int g = (wave * T::LA + d) / (BM / 8);
         char* sa = smem + slot * T::STAGE + (wave * T::LA + d) * 1024;
-        dma16(ra, sa, lane_kc < K - k0 - 64 * g ? a_off[d] + 2u * k0 : kOOB, 0u);
+        dma16(ra, sa, lane_kc < K - k0 - 64 * g ? a_off[d] : kOOB, 2u * k0);
       } else {
         const int j = d - T::LA;
         const int g = (wave * T::LB + j) / (BN / 8);
         char* sb = smem + slot * T::STAGE + T::A_BYTES + (wave * T::LB + j) * 1024;
-        dma16(rb, sb, lane_kc < K - k0 - 64 * g ? b_off[j] + 2u * k0 : kOOB, 0u);
+        dma16(rb, sb, lane_kc < K - k0 - 64 * g ? b_off[j] : kOOB, 2u * k0);
       }
     };
     auto issue = [&](int slot, int kt) {
@@ -132,25 +134,27 @@ __global__ void __launch_bounds__(WM* WN * 64, 1) gemm_dma_kernel(GemmArgs args)
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
     // One k-step: the FN x FM MFMAs on fragment buffer `buf`, with NR fragment reads (for the next
-    // k-step) and ND DMA loads (for a later K-tile) threaded between them, one per MFMA slot, the
-    // reads first. The order is pinned (sched_barrier) so the loads drain through the
+    // k-step) and ND DMA loads (for a later K-tile) threaded between them, each kind spread
+    // evenly over the MFMA slots. The order is pinned (sched_barrier) so the loads drain through the
     // vector-memory and LDS pipes while the MFMA pipe stays busy, instead of arriving in a burst.
     constexpr int NM = T::FN * T::FM;
     auto kstep = [&](int buf, auto zero_c, auto nr_c, auto nd_c, auto&& rd, auto&& dm) {
       constexpr bool kZero = decltype(zero_c)::value;
       constexpr int NR = decltype(nr_c)::value, ND = decltype(nd_c)::value;
-      static_assert(NR + ND <= 2 * NM, "at most two loads per MFMA slot");
+      static_assert(NR <= NM && ND <= NM, "at most one read and one DMA per MFMA slot");
       static_for<NM>([&](auto m_c) {
         constexpr int m = decltype(m_c)::value;
         constexpr int i = m / T::FM, j = m % T::FM;
         acc[i][j] = mfma16<TIn>(xf[buf][i], yf[buf][j], kZero ? zero4 : acc[i][j]);
-        // load slots: reads take slots 0 .. NR-1, DMAs the following ND (two per MFMA if needed)
-        constexpr int per = (NR + ND + NM - 1) / NM;
-        static_for<per>([&](auto q_c) {
-          constexpr int L = m * per + decltype(q_c)::value;
-          if constexpr (L < NR) rd(L);
-          else if constexpr (L < NR + ND) dm(L - NR);
-        });
+        // load slots: the reads, and separately the DMAs, are spread evenly over the MFMA slots
+        if constexpr (NR > 0) {
+          constexpr int sr = NM / NR;
+          if constexpr (m % sr == 0 && m / sr < NR) rd(m / sr);
+        }
+        if constexpr (ND > 0) {
+          constexpr int sd = NM / ND;
+          if constexpr (m % sd == sd / 2 && m / sd < ND) dm(m / sd);
+        }
         __builtin_amdgcn_sched_barrier(0);
       });
     };
@@ -159,16 +163,19 @@ __global__ void __launch_bounds__(WM* WN * 64, 1) gemm_dma_kernel(GemmArgs args)
     // One K-tile: k-steps 0 .. NSUB-1 of ring slot `slot`. Before the last k-step of every tile
     // but the last (kHandover, a compile-time flag so that the K-loop body is one straight-line
     // block whose accumulators never meet at a join): wait for tile k+1, sync, then (threaded through the MFMAs) read tile k+1's
-    // first fragments and refill `slot` with tile k+S. The refill is split in two halves so the
-    // loads spread over a whole K-tile: the first half in this hand-over k-step, the second half
-    // in k-step 0 of the next tile (kDefer). The slot stays free from this hand-over's barrier to
+    // first fragments and refill `slot` with tile k+S. With three or more stages the refill is
+    // split in two halves so the loads spread over a whole K-tile: the first half in this
+    // hand-over k-step, the second half in k-step 0 of the next tile (kDefer). The slot stays free from this hand-over's barrier to
     // the next one, and by the next hand-over every load of tile k+S has been issued, so the
     // vmcnt thresholds are unchanged. kFirst: the first tile, whose MFMA chains start from zero.
-    constexpr int LW1 = S > 1 ? T::LW / 2 : 0;  // refill loads issued in the hand-over k-step
+    // refill loads issued in the hand-over k-step: with two stages the whole refill goes there
+    // (the deferred half would land only one k-step before it is needed); with more stages it is
+    // split in half over two k-steps.
+    constexpr int LW1 = S > 2 ? T::LW / 2 : (S == 2 ? T::LW : 0);
     auto k_tile = [&](int k, int slot, auto first_c, auto handover_c) {
       constexpr bool kFirst = decltype(first_c)::value;
       constexpr bool kHandover = decltype(handover_c)::value;
-      constexpr bool kDefer = !kFirst && S > 1;
+      constexpr bool kDefer = !kFirst && S > 2;
       const int next_slot = slot + 1 == S ? 0 : slot + 1;
       const int prev_slot = slot == 0 ? S - 1 : slot - 1;
       static_for<T::NSUB>([&](auto sub_c) {
