@@ -10,8 +10,6 @@ output. One step is one gemm_run over operands already resident in HBM. Prints o
 from __future__ import annotations
 
 import argparse
-import glob
-import hashlib
 import json
 import os
 import sys
@@ -27,15 +25,6 @@ PEAK_HBM_GBS = 8000.0
 DTYPE_NAME = {0: "f16", 1: "bf16", 2: "f32"}
 
 
-def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "software_pipelined_tiled_amd", "csrc", "*"))):
-        with open(p, "rb") as f:
-            h.update(os.path.basename(p).encode())
-            h.update(f.read())
-    return h.hexdigest()[:16]
-
-
 def load_traffic(workload: str, shape_index: int, kernel: str) -> float | None:
     """HBM bytes per launch from the committed counter summary, if it matches these sources."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}_{shape_index}.json")
@@ -43,6 +32,8 @@ def load_traffic(workload: str, shape_index: int, kernel: str) -> float | None:
         return None
     with open(path) as f:
         d = json.load(f)
+    from software_pipelined_tiled_amd.profsum import kernel_source_hash
+
     if d.get("kernel_source_sha") != kernel_source_hash() or d.get("kernel") != kernel:
         return None
     return float(d["hbm_bytes_per_launch"])
@@ -54,15 +45,20 @@ def cpu_baseline(a_bits, b_bits, K, in_dt, out_dt, seconds: float) -> dict:
 
     threads = max(1, min(16, os.cpu_count() or 1))
     N = b_bits.shape[0]
-    rows = min(2 * threads, a_bits.shape[0])
-    t0 = time.perf_counter()
-    orc.gemm(a_bits[:rows], b_bits, K, in_dt, out_dt, threads=threads, want_sums=False)
-    t_probe = time.perf_counter() - t0
-    rows2 = int(max(rows, min(a_bits.shape[0], rows * seconds / max(t_probe, 1e-3))))
+
+    def timed(rows: int) -> float:
+        t0 = time.perf_counter()
+        orc.gemm(a_bits[:rows], b_bits, K, in_dt, out_dt, threads=threads, want_sums=False)
+        return time.perf_counter() - t0
+
+    # a call costs a fixed part (decoding B, starting threads) plus a part per row of A: fit both
+    # from two short calls, then size the sample to about `seconds`
+    r1, r2 = threads, 3 * threads
+    t1, t2 = timed(r1), timed(r2)
+    per_row = max((t2 - t1) / (r2 - r1), 1e-6)
+    rows2 = int(min(a_bits.shape[0], max(r2, (seconds - max(t1 - per_row * r1, 0.0)) / per_row)))
     rows2 = max(threads, (rows2 // threads) * threads)
-    t0 = time.perf_counter()
-    orc.gemm(a_bits[:rows2], b_bits, K, in_dt, out_dt, threads=threads, want_sums=False)
-    dt = time.perf_counter() - t0
+    dt = timed(rows2)
     return {"value": 2.0 * rows2 * N * K / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"rows 0..{rows2 - 1} of A against all {N} rows of B (K={K}); "
                       f"{2.0 * rows2 * N * K:.3e} flop in {dt:.2f} s, fp64 triple loop, {threads} threads"}
@@ -93,6 +89,7 @@ def main() -> int:
 
     import software_pipelined_tiled_amd as spt
     import synthetic_inputs as si
+    from software_pipelined_tiled_amd.profsum import kernel_source_hash
 
     torch.cuda.set_device(0)
     M, N, K, a_bits, b_bits, in_dt, out_dt = si.workload_operands(args.workload, args.shape_index)
@@ -131,7 +128,7 @@ def main() -> int:
     value = flop / (ms_per_step * 1e-3) / 1e12
     achieved = flop / (avg_launch_ms * 1e-3) / 1e12
     kernel_name = (f"gemm_{'dma' if desc['load_path'] == 1 else 'reg'}_kernel<{desc['bm']},{desc['bn']},"
-                   f"{desc['bk']},{desc['stages']},{DTYPE_NAME[in_dt]},{DTYPE_NAME[out_dt]}>")
+                   f"{desc['bk']},{desc['stages']},waves={desc['waves']},{DTYPE_NAME[in_dt]},{DTYPE_NAME[out_dt]}>")
     traffic = load_traffic(args.workload, args.shape_index, kernel_name)
     compulsory = (M * K + N * K) * 2 + M * N * (4 if out_dt == 2 else 2)
 

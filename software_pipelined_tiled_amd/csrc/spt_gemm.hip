@@ -162,15 +162,14 @@ __global__ void __launch_bounds__(WM* WN * 64, 1) gemm_dma_kernel(GemmArgs args)
 
     // One K-tile: k-steps 0 .. NSUB-1 of ring slot `slot`. Before the last k-step of every tile
     // but the last (kHandover, a compile-time flag so that the K-loop body is one straight-line
-    // block whose accumulators never meet at a join): wait for tile k+1, sync, then (threaded through the MFMAs) read tile k+1's
-    // first fragments and refill `slot` with tile k+S. With three or more stages the refill is
-    // split in two halves so the loads spread over a whole K-tile: the first half in this
-    // hand-over k-step, the second half in k-step 0 of the next tile (kDefer). The slot stays free from this hand-over's barrier to
-    // the next one, and by the next hand-over every load of tile k+S has been issued, so the
-    // vmcnt thresholds are unchanged. kFirst: the first tile, whose MFMA chains start from zero.
-    // refill loads issued in the hand-over k-step: with two stages the whole refill goes there
-    // (the deferred half would land only one k-step before it is needed); with more stages it is
-    // split in half over two k-steps.
+    // block whose accumulators never meet at a join): wait for tile k+1, sync, then, threaded
+    // through the MFMAs, read tile k+1's first fragments and refill `slot` with tile k+S.
+    // With two stages the whole refill goes into the hand-over k-step (LW1 = LW). With three or
+    // more it is split in half so the loads spread over a whole K-tile: the first half in the
+    // hand-over k-step, the second in k-step 0 of the next tile (kDefer). The slot stays free
+    // from this hand-over's barrier to the next one, and by the next hand-over every load of
+    // tile k+S has been issued, so the vmcnt thresholds are unchanged.
+    // kFirst: the first tile, whose MFMA chains start from zero.
     constexpr int LW1 = S > 2 ? T::LW / 2 : (S == 2 ? T::LW : 0);
     auto k_tile = [&](int k, int slot, auto first_c, auto handover_c) {
       constexpr bool kFirst = decltype(first_c)::value;

@@ -1,0 +1,191 @@
+"""Summaries of rocprofv3 CSV output for the GEMM kernels, as short text files.
+
+    python -m software_pipelined_tiled_amd.profsum kernel-stats STATS_CSV BENCH_JSON OUT_MD --command CMD
+        per-kernel durations (rocprofv3 --kernel-trace --stats --output-format csv) next to the
+        launch time the benchmark measured with HIP events in the same run
+
+    python -m software_pipelined_tiled_amd.profsum traffic FETCH_CSV WRITE_CSV BENCH_JSON OUT_JSON --command CMD
+        HBM bytes per GEMM launch from two counter runs (--pmc FETCH_SIZE, then --pmc WRITE_SIZE) of
+        `bench.py --copy-calibration`. Each counter is scaled by what it reads for the 1 GiB copy
+        kernel launched in the same run (which moves exactly 2^30 bytes each way).
+
+    python -m software_pipelined_tiled_amd.profsum lds COUNTER_CSV OUT_MD --command CMD
+        bank-conflict ratio SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE of each LDS read-pattern probe
+        launched by `python3 -m software_pipelined_tiled_amd.probes lds` (swizzles -1, 0 .. 4 in order)
+
+BENCH_JSON is a file whose last line is the JSON line bench.py printed in that run.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import re
+import statistics
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+COPY_BYTES = 1 << 30
+
+
+def _code_tokens(text: str) -> str:
+    """Source text without comments and whitespace runs: what the compiler sees."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
+def kernel_source_hash() -> str:
+    """Hash of the kernel sources' code (comments and layout ignored); a traffic figure is only
+    valid for the code it was taken on."""
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(HERE, "csrc", "*"))):
+        with open(p, encoding="utf-8") as f:
+            h.update(os.path.basename(p).encode())
+            h.update(_code_tokens(f.read()).encode())
+    return h.hexdigest()[:16]
+
+
+def kernel_prefix(plan: dict) -> str:
+    """Start of the demangled template name of the kernel a plan launches."""
+    kind = "dma" if plan["load_path"] == 1 else "reg"
+    return f"gemm_{kind}_kernel<{plan['bm']}, {plan['bn']}, {plan['bk']}, "
+
+
+def _bench_line(path: str) -> dict:
+    with open(path) as f:
+        lines = [l for l in f.read().splitlines() if l.strip().startswith("{")]
+    if not lines:
+        raise SystemExit(f"no JSON line in {path}")
+    return json.loads(lines[-1])
+
+
+def _rows(path: str) -> list[dict]:
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def kernel_stats(stats_csv: str, bench_json: str, out_md: str, command: str) -> None:
+    line = _bench_line(bench_json)
+    plan = line["config"]["plan"]
+    rows = _rows(stats_csv)
+    pre = kernel_prefix(plan)
+    out = [f"# Kernel durations: {line['config']['workload']} ({line['config']['M']}x{line['config']['N']}x"
+           f"{line['config']['K']}, {line['config']['in_dtype']} -> {line['config']['out_dtype']})", "",
+           f"Command: `{command}`", "",
+           f"Plan: {json.dumps(plan)}", "",
+           "| kernel | calls | average (us) | min (us) | max (us) | share of GPU time |",
+           "|---|---|---|---|---|---|"]
+    gemm_avg = None
+    for r in rows:
+        name = r.get("Name", r.get("KernelName", "?"))
+        avg = float(r["AverageNs"]) / 1e3
+        out.append(f"| `{name[:110]}` | {r['Calls']} | {avg:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
+                   f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
+        if pre in name:
+            gemm_avg = avg
+    ev_us = line["extra"]["avg_launch_ms"] * 1e3
+    out += ["", f"GEMM launch time from HIP events in the same run: {ev_us:.1f} us "
+                f"(rocprofv3 average {gemm_avg:.1f} us, ratio {ev_us / gemm_avg:.3f})." if gemm_avg else
+            f"GEMM launch time from HIP events: {ev_us:.1f} us (kernel not found in the stats).",
+            f"Throughput reported by bench.py in this run: {line['value']:.1f} TFLOP/s "
+            f"(roofline.achieved {line['roofline']['achieved']:.1f} TFLOP/s, frac {line['roofline']['frac']:.3f})."]
+    with open(out_md, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print("\n".join(out))
+
+
+def _counter_means(path: str, counter: str, pre: str) -> tuple[float, float, int]:
+    """Mean per-dispatch value (bytes) of `counter` for the GEMM (skipping its first, cold launch)
+    and for the copy kernel."""
+    gemm, copy = [], []
+    for r in _rows(path):
+        if r["Counter_Name"] != counter:
+            continue
+        v = float(r["Counter_Value"]) * 1024.0  # rocprofv3 reports these two counters in KiB
+        if pre in r["Kernel_Name"]:
+            gemm.append(v)
+        elif "copy16_kernel" in r["Kernel_Name"]:
+            copy.append(v)
+    if len(gemm) < 2 or not copy:
+        raise SystemExit(f"{path}: need >= 2 GEMM and >= 1 copy dispatches with {counter}")
+    return statistics.mean(gemm[1:]), statistics.mean(copy), len(gemm) - 1
+
+
+def traffic(fetch_csv: str, write_csv: str, bench_json: str, out_json: str, command: str) -> None:
+    line = _bench_line(bench_json)
+    plan = line["config"]["plan"]
+    pre = kernel_prefix(plan)
+    f_gemm, f_copy, nf = _counter_means(fetch_csv, "FETCH_SIZE", pre)
+    w_gemm, w_copy, nw = _counter_means(write_csv, "WRITE_SIZE", pre)
+    f_scale, w_scale = COPY_BYTES / f_copy, COPY_BYTES / w_copy
+    c = line["config"]
+    out_bytes = 4 if c["out_dtype"] == "f32" else 2
+    compulsory = (c["M"] * c["K"] + c["N"] * c["K"]) * 2 + c["M"] * c["N"] * out_bytes
+    read, write = f_gemm * f_scale, w_gemm * w_scale
+    d = {"workload": c["workload"], "kernel": c["kernel"], "kernel_source_sha": kernel_source_hash(),
+         "hbm_bytes_per_launch": read + write, "read_bytes_per_launch": read, "write_bytes_per_launch": write,
+         "compulsory_bytes": compulsory, "traffic_over_compulsory": (read + write) / compulsory,
+         "fetch_scale": f_scale, "write_scale": w_scale, "gemm_dispatches_averaged": [nf, nw],
+         "raw_fetch_size_kib_per_launch": f_gemm / 1024, "raw_write_size_kib_per_launch": w_gemm / 1024,
+         "raw_copy_fetch_kib": f_copy / 1024, "raw_copy_write_kib": w_copy / 1024, "command": command}
+    with open(out_json, "w") as f:
+        json.dump(d, f, indent=1)
+        f.write("\n")
+    print(json.dumps(d, indent=1))
+
+
+LDS_PATTERNS = {-1: "linear 16*lane (reference)", 0: "none (f = 0)", 1: "row % 8 (the pages' 128-byte swizzle)",
+                2: "(row % 8) XOR bit3(row)", 3: "(row / 2) % 8", 4: "(row % 4) XOR (bit2(row) << 2)"}
+
+
+def lds(counter_csv: str, out_md: str, command: str) -> None:
+    per = {}
+    for r in _rows(counter_csv):
+        if "lds_read_kernel" not in r["Kernel_Name"]:
+            continue
+        per.setdefault(int(r["Dispatch_Id"]), {})[r["Counter_Name"]] = float(r["Counter_Value"])
+    order = sorted(per)
+    if len(order) != len(LDS_PATTERNS):
+        raise SystemExit(f"expected {len(LDS_PATTERNS)} probe dispatches, found {len(order)}")
+    out = ["# LDS bank conflicts of the MFMA operand read pattern on gfx950", "",
+           "Pattern: one ds_read_b128 per lane; lane l reads row l%16 of a tile with 128-byte rows, at logical",
+           "16-byte chunk l/16, stored at physical chunk = chunk XOR f(row). One workgroup of 4 waves per CU.",
+           "Ratio = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE (0 = conflict-free, 0.5 = 2-way, 0.75 = 4-way).", "",
+           f"Command: `{command}`", "",
+           "| f(row) | SQ_LDS_BANK_CONFLICT | SQ_LDS_IDX_ACTIVE | ratio |", "|---|---|---|---|"]
+    for sw, d in zip(LDS_PATTERNS, order):
+        c, a = per[d].get("SQ_LDS_BANK_CONFLICT", 0.0), per[d].get("SQ_LDS_IDX_ACTIVE", 0.0)
+        out.append(f"| {LDS_PATTERNS[sw]} | {c:.4g} | {a:.4g} | {c / a if a else float('nan'):.3f} |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print("\n".join(out))
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = ap.add_subparsers(dest="what", required=True)
+    k = sub.add_parser("kernel-stats")
+    k.add_argument("stats_csv"), k.add_argument("bench_json"), k.add_argument("out_md")
+    k.add_argument("--command", required=True)
+    t = sub.add_parser("traffic")
+    t.add_argument("fetch_csv"), t.add_argument("write_csv"), t.add_argument("bench_json"), t.add_argument("out_json")
+    t.add_argument("--command", required=True)
+    d = sub.add_parser("lds")
+    d.add_argument("counter_csv"), d.add_argument("out_md")
+    d.add_argument("--command", required=True)
+    a = ap.parse_args(argv)
+    if a.what == "lds":
+        lds(a.counter_csv, a.out_md, a.command)
+    elif a.what == "kernel-stats":
+        kernel_stats(a.stats_csv, a.bench_json, a.out_md, a.command)
+    else:
+        traffic(a.fetch_csv, a.write_csv, a.bench_json, a.out_json, a.command)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
