@@ -89,7 +89,7 @@ def main() -> int:
 
     import software_pipelined_tiled_amd as spt
     import synthetic_inputs as si
-    from software_pipelined_tiled_amd.profsum import kernel_source_hash
+    from software_pipelined_tiled_amd.profsum import kernel_label, kernel_source_hash
 
     torch.cuda.set_device(0)
     M, N, K, a_bits, b_bits, in_dt, out_dt = si.workload_operands(args.workload, args.shape_index)
@@ -127,8 +127,7 @@ def main() -> int:
     flop = 2.0 * M * N * K
     value = flop / (ms_per_step * 1e-3) / 1e12
     achieved = flop / (avg_launch_ms * 1e-3) / 1e12
-    kernel_name = (f"gemm_{'dma' if desc['load_path'] == 1 else 'reg'}_kernel<{desc['bm']},{desc['bn']},"
-                   f"{desc['bk']},{desc['stages']},waves={desc['waves']},{DTYPE_NAME[in_dt]},{DTYPE_NAME[out_dt]}>")
+    kernel_name = kernel_label(desc, DTYPE_NAME[in_dt], DTYPE_NAME[out_dt])
     traffic = load_traffic(args.workload, args.shape_index, kernel_name)
     compulsory = (M * K + N * K) * 2 + M * N * (4 if out_dt == 2 else 2)
 

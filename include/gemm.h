@@ -56,9 +56,13 @@ typedef enum {
 /*
  * Kernel configuration. gemm_plan_create takes an optional override (NULL = heuristic);
  * gemm_plan_describe reports the configuration a plan will launch.
- *   bm, bn, bk   output tile (bm x bn) and K-tile depth; bk is 64 or 128
- *   stages       S, LDS ring depth (1 = serial: wait for a tile, compute it, then load the next)
- *   waves        wavefronts per workgroup (64 lanes each)
+ *   bm, bn, bk   output tile (bm x bn) and K-tile depth; bk is 32, 64 or 128
+ *   stages       S, LDS ring depth (1 = serial: wait for a tile, compute it, then load the next).
+ *                With bk 64 and a square tile, 5 means a split ring of five operand slots, each
+ *                holding one A or one B K-tile (two and a half stages)
+ *   waves        wavefronts per workgroup (64 lanes each); 8 selects the two-wave-group kernel
+ *                (256x256, bk 64, stages 2 or 5), where one group of four waves runs MFMAs while
+ *                the other issues loads, alternating at workgroup barriers
  *   mfma         MFMA shape: 16 = v_mfma_f32_16x16x32_{f16,bf16}
  *   persistent   1: launch min(#tiles, grid) workgroups that loop over tiles; 0: one per tile
  *   group_m      grouped raster height, in tiles (tiles sharing A row bands run back to back)
@@ -139,9 +143,10 @@ int gemm_schedule_tile(int64_t tiles_m, int64_t tiles_n, int group_m, int grid, 
                        int64_t* tm, int64_t* tn);
 
 /*
- * Byte offset, inside one LDS operand tile of `rows` rows and depth bk (64 or 128), of the
- * 16-byte chunk holding elements [8*chunk, 8*chunk + 8) of tile row `row` (the XOR swizzle).
- * Returns -1 for invalid arguments.
+ * Byte offset, inside one LDS operand tile of `rows` rows and depth bk (32, 64 or 128), of the
+ * 16-byte chunk holding elements [8*chunk, 8*chunk + 8) of tile row `row` (the XOR swizzle:
+ * 128-byte rows with chunk XOR (row mod 8) for bk 64 and 128, 64-byte rows with chunk XOR
+ * ((row / 4) mod 4) for bk 32). Returns -1 for invalid arguments.
  */
 int64_t gemm_lds_chunk_offset(int rows, int bk, int row, int chunk);
 

@@ -57,8 +57,21 @@ const spt::KernelEntry* find_entry(const spt::KernelEntry* t, int n, const gemm_
 
 const spt::KernelEntry* find_entry_for_path(const gemm_config_t& c) {
   int n = 0;
-  const spt::KernelEntry* t = c.load_path == GEMM_LOAD_REG ? spt::reg_kernel_table(&n) : spt::dma_kernel_table(&n);
+  if (c.load_path == GEMM_LOAD_REG) {
+    const spt::KernelEntry* t = spt::reg_kernel_table(&n);
+    return find_entry(t, n, c);
+  }
+  const spt::KernelEntry* t = spt::dma_kernel_table(&n);
+  if (const spt::KernelEntry* e = find_entry(t, n, c)) return e;
+  t = spt::pp_kernel_table(&n);
   return find_entry(t, n, c);
+}
+
+// LDS bytes of a configuration's ring: S stages of an A and a B K-tile, or, for the split ring
+// (bk 64, five slots, square tile), five operand slots of one K-tile each.
+int ring_bytes(const gemm_config_t& c) {
+  const bool split = c.load_path != GEMM_LOAD_REG && c.bk == 64 && c.stages == 5 && c.bm == c.bn;
+  return split ? c.stages * c.bm * c.bk * 2 : c.stages * (c.bm + c.bn) * c.bk * 2;
 }
 
 bool dma_eligible(int64_t K, int64_t lda, int64_t ldb) { return K % 8 == 0 && lda % 8 == 0 && ldb % 8 == 0; }
@@ -72,10 +85,11 @@ int groups_per_cu(const gemm_config_t& c, int lds_bytes) {
   return g < 1 ? 1 : g;
 }
 
-// Preferred tiles, largest first; the first that yields at least one tile per CU wins.
-struct Candidate { int bm, bn, bk, stages; };
-const Candidate kDmaMenu[] = {{256, 256, 64, 2}, {256, 128, 64, 3}, {128, 128, 64, 4}, {64, 64, 64, 4}};
-const Candidate kRegMenu[] = {{128, 128, 64, 2}, {64, 64, 64, 2}};
+// Preferred tiles, largest first; the first that yields at least one tile per CU wins. The 256x256
+// tile runs on the two-wave-group kernel (8 waves) with the split ring of five operand slots.
+struct Candidate { int bm, bn, bk, stages, waves; };
+const Candidate kDmaMenu[] = {{256, 256, 64, 5, 8}, {256, 128, 64, 3, 4}, {128, 128, 64, 4, 4}, {64, 64, 64, 4, 4}};
+const Candidate kRegMenu[] = {{128, 128, 64, 2, 4}, {64, 64, 64, 2, 4}};
 
 gemm_config_t choose(int64_t M, int64_t N, const Candidate* menu, int n, int path, int cu_count, int lds_bytes) {
   gemm_config_t best{};
@@ -84,9 +98,9 @@ gemm_config_t choose(int64_t M, int64_t N, const Candidate* menu, int n, int pat
     const Candidate& c = menu[i];
     const int64_t tiles = ceil_div(M, c.bm) * ceil_div(N, c.bn);
     gemm_config_t cfg{};
-    cfg.bm = c.bm; cfg.bn = c.bn; cfg.bk = c.bk; cfg.stages = c.stages; cfg.waves = 4; cfg.mfma = 16;
+    cfg.bm = c.bm; cfg.bn = c.bn; cfg.bk = c.bk; cfg.stages = c.stages; cfg.waves = c.waves; cfg.mfma = 16;
     cfg.persistent = 1; cfg.group_m = 8; cfg.load_path = path;
-    cfg.lds_bytes = c.stages * (c.bm + c.bn) * c.bk * 2;
+    cfg.lds_bytes = ring_bytes(cfg);
     if (tiles >= cu_count) return cfg;
     if (tiles > best_tiles) { best = cfg; best_tiles = tiles; }
   }
@@ -97,7 +111,7 @@ void finish_config(gemm_config_t& c, int64_t M, int64_t N, int cu_count, int lds
   tm = (int)ceil_div(M, c.bm);
   tn = (int)ceil_div(N, c.bn);
   const int64_t tiles = (int64_t)tm * tn;
-  c.lds_bytes = c.stages * (c.bm + c.bn) * c.bk * 2;
+  c.lds_bytes = ring_bytes(c);
   if (c.group_m < 1) c.group_m = 8;
   if (c.persistent) {
     int64_t g = c.grid > 0 ? c.grid : (int64_t)cu_count * groups_per_cu(c, lds_bytes);
@@ -130,7 +144,7 @@ gemm_status_t select_impl(int64_t M, int64_t N, int64_t K, gemm_dtype_t a, gemm_
     if (cfg.mfma == 0) cfg.mfma = 16;
     if (cfg.load_path == GEMM_LOAD_AUTO) cfg.load_path = dma_ok ? GEMM_LOAD_DMA : GEMM_LOAD_REG;
     if (cfg.load_path == GEMM_LOAD_DMA && !dma_ok) return GEMM_ERR_INVALID;
-    cfg.lds_bytes = cfg.stages * (cfg.bm + cfg.bn) * cfg.bk * 2;
+    cfg.lds_bytes = ring_bytes(cfg);
     if (!find_entry_for_path(cfg)) return GEMM_ERR_INVALID;
     if (cfg.lds_bytes > lds_bytes) return GEMM_ERR_INVALID;
   } else if (dma_ok) {
@@ -271,8 +285,9 @@ int gemm_schedule_tile(int64_t tiles_m, int64_t tiles_n, int group_m, int grid, 
 }
 
 int64_t gemm_lds_chunk_offset(int rows, int bk, int row, int chunk) {
-  if ((bk != 64 && bk != 128) || rows < 1 || row < 0 || row >= rows || chunk < 0 || chunk >= bk / 8) return -1;
-  return spt::lds_chunk_offset(rows, row, chunk);
+  if ((bk != 32 && bk != 64 && bk != 128) || rows < 1 || row < 0 || row >= rows || chunk < 0 || chunk >= bk / 8)
+    return -1;
+  return spt::lds_chunk_offset(rows, row, chunk, bk);
 }
 
 }  // extern "C"

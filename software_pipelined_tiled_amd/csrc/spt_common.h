@@ -51,10 +51,17 @@ SPT_HD void grouped_raster(int t, int tiles_m, int tiles_n, int group_m, int& tm
 // f(r) = r mod 8, the pages' 128-byte swizzle. Measured on gfx950 with SQ_LDS_BANK_CONFLICT
 // for the MFMA operand read (16 consecutive rows at one chunk per 64-lane ds_read_b128), it is
 // conflict-free, where the unswizzled layout is 4-way conflicted.
+//
+// A 32-element K-tile has 64-byte rows of four chunks (the pages' narrower swizzle widths for a
+// box under 128 bytes). There f(r) = (r / 4) mod 4: the 16 rows one MFMA operand read touches
+// then fall on 16 distinct 16-byte bank groups of a 256-byte window for every chunk, so the read
+// is conflict-free however the hardware splits the 64 lanes into passes.
 SPT_HD int swz(int r) { return r & 7; }
+SPT_HD int swz64(int r) { return (r >> 2) & 3; }
 
-// byte offset of logical chunk c (0 .. BK/8-1) of row r in an R-row tile
-SPT_HD int lds_chunk_offset(int R, int r, int c) {
+// byte offset of logical chunk c (0 .. BK/8-1) of row r in an R-row tile with K-tile depth bk
+SPT_HD int lds_chunk_offset(int R, int r, int c, int bk = 64) {
+  if (bk == 32) return r * 64 + (((c & 3) ^ swz64(r)) << 4);
   return (c >> 3) * (R * 128) + r * 128 + (((c & 7) ^ swz(r)) << 4);
 }
 

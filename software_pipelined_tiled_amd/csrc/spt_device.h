@@ -58,6 +58,44 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, unsig
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, voffset, soffset, 0, 0);
 }
 
+// The same load issued through inline assembly (the LDS address travels in M0), so the compiler
+// does not see an LDS write: otherwise it guards every later LDS read that might alias the
+// destination with a wait for this load, which serialises fragment reads behind the loads in
+// flight. A kernel using it orders its LDS reads after its own loads explicitly (s_waitcnt vmcnt,
+// then s_barrier) before any wave reads a tile.
+__device__ __forceinline__ void dma16_unseen(__amdgpu_buffer_rsrc_t r, void* lds, unsigned voffset,
+                                             unsigned soffset) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(lds_void_t*)lds);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(m0), "v"(voffset), "s"(r), "s"(soffset)
+               : "memory", "m0");
+}
+
+// v + c (c wave-uniform), computed where it is written: the compiler may not hoist it, so a loop
+// that issues many loads keeps one temporary instead of one precomputed register per load.
+__device__ __forceinline__ unsigned add_in_place(unsigned v, unsigned c) {
+  unsigned r;
+  asm volatile("v_add_u32 %0, %1, %2" : "=v"(r) : "s"(c), "v"(v));
+  return r;
+}
+
+// x, through a move the compiler cannot see into: values derived from the result are computed
+// after this point rather than hoisted above it.
+__device__ __forceinline__ unsigned opaque_u32(unsigned x) {
+  unsigned r;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "v"(x));
+  return r;
+}
+
+// The same for a wave-uniform value (kept in a scalar register). Used for ring offsets, so the
+// compiler does not turn every address derived from them into an induction variable of its own.
+__device__ __forceinline__ int opaque_s32(int x) {
+  int r;
+  asm volatile("s_mov_b32 %0, %1" : "=s"(r) : "s"(x));
+  return r;
+}
+
 // static_for<N>(f): f(std::integral_constant<int, 0>{}) ... f(std::integral_constant<int, N-1>{}),
 // so loop indices that select code paths are compile-time constants.
 template <typename F, int... I>
@@ -131,6 +169,27 @@ __device__ __forceinline__ void store8(const float (&v)[8], __amdgpu_buffer_rsrc
   }
 }
 
+// Store the 8 consecutive outputs v[0..7] at byte offset voffset + soffset of `rc` (an interior
+// segment: no masking).
+template <int OUT>
+__device__ __forceinline__ void store8_at(const float (&v)[8], __amdgpu_buffer_rsrc_t rc, unsigned voffset,
+                                         unsigned soffset) {
+  if constexpr (OUT == 2) {
+    u32x4 lo = {__builtin_bit_cast(unsigned, v[0]), __builtin_bit_cast(unsigned, v[1]),
+                __builtin_bit_cast(unsigned, v[2]), __builtin_bit_cast(unsigned, v[3])};
+    u32x4 hi = {__builtin_bit_cast(unsigned, v[4]), __builtin_bit_cast(unsigned, v[5]),
+                __builtin_bit_cast(unsigned, v[6]), __builtin_bit_cast(unsigned, v[7])};
+    __builtin_amdgcn_raw_buffer_store_b128(lo, rc, voffset, soffset, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(hi, rc, voffset, soffset + 16u, 0);
+  } else {
+    unsigned p[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) p[e] = OUT == 1 ? pack_bf16(v[2 * e], v[2 * e + 1]) : pack_f16(v[2 * e], v[2 * e + 1]);
+    u32x4 q = {p[0], p[1], p[2], p[3]};
+    __builtin_amdgcn_raw_buffer_store_b128(q, rc, voffset, soffset, 0);
+  }
+}
+
 // ------------------------------------------------------------------------------ the kernel
 template <int BM, int BN, int BK, int S, int WM, int WN>
 struct TileShape {
@@ -138,18 +197,30 @@ struct TileShape {
   static constexpr int TM = BM / WM, TN = BN / WN;  // wave tile
   static constexpr int FM = TM / 16, FN = TN / 16;  // 16-row fragments per wave (A side, B side)
   static constexpr int NSUB = BK / 32;              // MFMA k-steps per K-tile
+  // LDS rows: 64-element groups of 128-byte rows, or one 64-byte row for a 32-deep K-tile
+  static constexpr int GK = BK == 32 ? 32 : 64;     // elements per LDS row
+  static constexpr int RB = 2 * GK;                 // bytes per LDS row
+  static constexpr int CPR = RB / 16;               // 16-byte chunks per row
+  static constexpr int RPI = 1024 / RB;             // rows one DMA instruction fills
+  static constexpr int FRAG = 16 * RB;              // bytes between consecutive 16-row fragments
   static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2, STAGE = A_BYTES + B_BYTES;
-  static constexpr int LDS = S * STAGE;
+  // Split ring (S = 5 with 64-deep K-tiles): five operand slots; K-tile k's A tile sits in slot
+  // 2k mod 5 and its B tile in slot 2k+1 mod 5, i.e. two and a half stages.
+  static constexpr bool SPLIT = BK == 64 && S == 5;
+  static constexpr int SLOT = A_BYTES;
+  static constexpr int LDS = SPLIT ? S * SLOT : S * STAGE;
   static constexpr int A_INSTR = A_BYTES / 1024, B_INSTR = B_BYTES / 1024;  // 1 KiB per DMA instruction
   static constexpr int LA = A_INSTR / W, LB = B_INSTR / W, LW = LA + LB;   // per wave, per stage
-  static_assert(BK == 64 || BK == 128, "K-tile is one or two 128-byte swizzle groups");
-  static_assert(S >= 1 && S <= 4, "1..4 stages");
+  static constexpr int MAX_VM = SPLIT ? 2 * LA + LB : LW * (S > 1 ? S - 1 : 1);  // largest vmcnt threshold
+  static_assert(BK == 32 || BK == 64 || BK == 128, "K-tile is one 64-byte row or one or two 128-byte groups");
+  static_assert(S >= 1 && S <= (BK == 128 ? 4 : 5), "1..4 stages (5 slots for 32- or 64-deep K-tiles)");
+  static_assert(!SPLIT || A_BYTES == B_BYTES, "split ring: A and B tiles fill equal slots");
   static_assert(TM % 16 == 0 && TN % 32 == 0, "wave tile: 16-row A fragments, pairs of 16-row B fragments");
   static_assert(A_INSTR % W == 0 && B_INSTR % W == 0, "every wave issues the same number of loads");
-  static_assert(BM % 8 == 0 && BN % 32 == 0, "tile rows");
-  static_assert(LW * (S > 1 ? S - 1 : 1) < 64, "vmcnt thresholds fit the 6-bit counter");
+  static_assert(BM % RPI == 0 && BN % 32 == 0, "tile rows");
+  static_assert(MAX_VM < 64, "vmcnt thresholds fit the 6-bit counter");
   static_assert(LDS <= 160 * 1024, "LDS ring fits the 160 KiB of a CU");
-  static_assert(NSUB % 2 == 0, "fragment double buffer parity");
+  static_assert(NSUB % 2 == 0 || NSUB == 1, "fragment double buffer parity");
 };
 
 }  // namespace spt

@@ -24,6 +24,10 @@
 
 namespace spt {
 
+struct Regions {
+  int a, b;  // LDS byte offsets of a K-tile's A and B tiles
+};
+
 template <int BM, int BN, int BK, int S, int WM, int WN, typename TIn, int OUT>
 __global__ void __launch_bounds__(WM* WN * 64, 1) gemm_dma_kernel(GemmArgs args) {
   using T = TileShape<BM, BN, BK, S, WM, WN>;
@@ -36,28 +40,45 @@ __global__ void __launch_bounds__(WM* WN * 64, 1) gemm_dma_kernel(GemmArgs args)
   const int KT = (K + BK - 1) / BK;
 
   // DMA address map. A instruction j of this wave fills LDS bytes [(wave*LA + j) * 1024, +1024)
-  // of the stage's A region: rows rho = 8*rb + lane/8 of 64-wide group g; the lane's physical
-  // chunk lane%8 must hold logical chunk (lane%8) XOR swz(rho). The swizzle has period 8 in the
-  // row, so swz(rho) = swz(lane/8) and the chunk depends on the lane alone; the group g is
-  // wave-uniform. Element offset of the lane's chunk inside the K-tile: 64*g + lane_kc.
-  const int lane_kc = 8 * ((lane & 7) ^ swz(lane >> 3));
+  // of the stage's A region: rows rho = RPI*rb + lane/CPR of row group g (RPI = 8 rows of 128
+  // bytes, or 16 rows of 64 bytes for a 32-deep K-tile); the lane's physical chunk lane%CPR must
+  // hold logical chunk (lane%CPR) XOR swizzle(rho). The swizzle has period RPI in the row, so it
+  // depends on lane/CPR alone and the chunk depends on the lane alone; the group g is
+  // wave-uniform. Element offset of the lane's chunk inside the K-tile: GK*g + lane_kc.
+  const int lane_kc = T::RB == 128 ? 8 * ((lane & 7) ^ swz(lane >> 3)) : 8 * ((lane & 3) ^ swz64(lane >> 2));
   auto a_map = [&](int j, int& row, int& g) {
-    const int q = wave * T::LA + j, rb = q % (BM / 8);
-    g = q / (BM / 8);
-    row = 8 * rb + (lane >> 3);
+    const int q = wave * T::LA + j, rb = q % (BM / T::RPI);
+    g = q / (BM / T::RPI);
+    row = T::RPI * rb + lane / T::CPR;
   };
   auto b_map = [&](int j, int& row, int& g) {
-    const int q = wave * T::LB + j, rb = q % (BN / 8);
-    g = q / (BN / 8);
-    row = b_row_perm(8 * rb + (lane >> 3));
+    const int q = wave * T::LB + j, rb = q % (BN / T::RPI);
+    g = q / (BN / T::RPI);
+    row = b_row_perm(T::RPI * rb + lane / T::CPR);
   };
-  // fragment read offsets for k-step `sub` at f = 0 (fragment f adds 16 rows = 2048 bytes)
+  // fragment read offsets for k-step `sub` at f = 0 (fragment f adds 16 rows = FRAG bytes)
   int a_rd[T::NSUB], b_rd[T::NSUB];
 #pragma unroll
   for (int s = 0; s < T::NSUB; ++s) {
-    a_rd[s] = lds_chunk_offset(BM, wm * T::TM + (lane & 15), 4 * s + (lane >> 4));
-    b_rd[s] = T::A_BYTES + lds_chunk_offset(BN, wn * T::TN + (lane & 15), 4 * s + (lane >> 4));
+    a_rd[s] = lds_chunk_offset(BM, wm * T::TM + (lane & 15), 4 * s + (lane >> 4), BK);
+    b_rd[s] = lds_chunk_offset(BN, wn * T::TN + (lane & 15), 4 * s + (lane >> 4), BK);
   }
+
+  // Ring positions. Plain ring: position = stage, the A tile at its start and the B tile after it.
+  // Split ring: position = the A tile's slot; the B tile is in the next slot, and the next K-tile
+  // starts two slots on.
+  auto regions = [&](int pos) {
+    if constexpr (T::SPLIT) return Regions{pos * T::SLOT, (pos + 1 == S ? 0 : pos + 1) * T::SLOT};
+    else return Regions{pos * T::STAGE, pos * T::STAGE + T::A_BYTES};
+  };
+  auto pos_next = [&](int pos) {
+    if constexpr (T::SPLIT) return pos + 2 >= S ? pos + 2 - S : pos + 2;
+    else return pos + 1 == S ? 0 : pos + 1;
+  };
+  auto pos_prev = [&](int pos) {
+    if constexpr (T::SPLIT) return pos < 2 ? pos + S - 2 : pos - 2;
+    else return pos == 0 ? S - 1 : pos - 1;
+  };
 
   const int u = xcd_remap(blockIdx.x, args.grid);
   bool first_tile = true;
@@ -79,52 +100,51 @@ __global__ void __launch_bounds__(WM* WN * 64, 1) gemm_dma_kernel(GemmArgs args)
     for (int j = 0; j < T::LA; ++j) {
       int row, g;
       a_map(j, row, g);
-      a_off[j] = row < rows_left ? (unsigned)(row * args.lda + 64 * g + lane_kc) * 2u : kOOB;
+      a_off[j] = row < rows_left ? (unsigned)(row * args.lda + T::GK * g + lane_kc) * 2u : kOOB;
     }
 #pragma unroll
     for (int j = 0; j < T::LB; ++j) {
       int row, g;
       b_map(j, row, g);
-      b_off[j] = row < cols_left ? (unsigned)(row * args.ldb + 64 * g + lane_kc) * 2u : kOOB;
+      b_off[j] = row < cols_left ? (unsigned)(row * args.ldb + T::GK * g + lane_kc) * 2u : kOOB;
     }
 
     // DMA instruction d (0 .. LW-1: A loads first, then B) of this wave's share of K-tile kt,
     // into ring slot `slot`. The K offset rides in the scalar soffset; the per-lane voffset is a
     // constant, replaced by one past num_records (reads zero) when the lane's chunk lies at or past
-    // K (lane_kc >= K - k0 - 64*g: one compare per group and K-tile). K-tiles past the end are
+    // K (lane_kc >= K - k0 - GK*g: one compare per group and K-tile). K-tiles past the end are
     // therefore zero-filling dummies, and every hand-over issues exactly LW loads per wave, which
     // keeps every vmcnt threshold constant. (kOOB + soffset stays past num_records: soffset < 2^31.)
-    auto dma_one = [&](int slot, int kt, int d) {
+    // `dst` gives the LDS byte offsets of the A and B tiles' destinations.
+    auto dma_one = [&](Regions dst, int kt, int d) {
       const int k0 = kt * BK;
       if (d < T::LA) {
-        const int g = (wave * T::LA + d) / (BM / 8);
-        char* sa = smem + slot * T::STAGE + (wave * T::LA + d) * 1024;
-        dma16(ra, sa, lane_kc < K - k0 - 64 * g ? a_off[d] : kOOB, 2u * k0);
+        const int g = (wave * T::LA + d) / (BM / T::RPI);
+        char* sa = smem + dst.a + (wave * T::LA + d) * 1024;
+        dma16(ra, sa, lane_kc < K - k0 - T::GK * g ? a_off[d] : kOOB, 2u * k0);
       } else {
         const int j = d - T::LA;
-        const int g = (wave * T::LB + j) / (BN / 8);
-        char* sb = smem + slot * T::STAGE + T::A_BYTES + (wave * T::LB + j) * 1024;
-        dma16(rb, sb, lane_kc < K - k0 - 64 * g ? b_off[j] : kOOB, 2u * k0);
+        const int g = (wave * T::LB + j) / (BN / T::RPI);
+        char* sb = smem + dst.b + (wave * T::LB + j) * 1024;
+        dma16(rb, sb, lane_kc < K - k0 - T::GK * g ? b_off[j] : kOOB, 2u * k0);
       }
     };
-    auto issue = [&](int slot, int kt) {
+    auto issue = [&](Regions dst, int kt) {
 #pragma unroll
-      for (int d = 0; d < T::LW; ++d) dma_one(slot, kt, d);
+      for (int d = 0; d < T::LW; ++d) dma_one(dst, kt, d);
     };
 
     u32x4 xf[2][T::FN], yf[2][T::FM];  // fragment double buffer: B side (x), A side (y)
     // fragment r of k-step `sub` (r < FN: B side, else A side) into buffer `buf`
-    auto read_frag = [&](int slot, int sub, int buf, int r) {
-      const char* base = smem + slot * T::STAGE;
-      if (r < T::FN) xf[buf][r] = *(const u32x4*)(base + b_rd[sub] + r * 2048);
-      else yf[buf][r - T::FN] = *(const u32x4*)(base + a_rd[sub] + (r - T::FN) * 2048);
+    auto read_frag = [&](Regions src, int sub, int buf, int r) {
+      if (r < T::FN) xf[buf][r] = *(const u32x4*)(smem + src.b + b_rd[sub] + r * T::FRAG);
+      else yf[buf][r - T::FN] = *(const u32x4*)(smem + src.a + a_rd[sub] + (r - T::FN) * T::FRAG);
     };
-    auto read_frags = [&](int slot, int sub, int buf) {
-      const char* base = smem + slot * T::STAGE;
+    auto read_frags = [&](Regions src, int sub, int buf) {
 #pragma unroll
-      for (int f = 0; f < T::FN; ++f) xf[buf][f] = *(const u32x4*)(base + b_rd[sub] + f * 2048);
+      for (int f = 0; f < T::FN; ++f) xf[buf][f] = *(const u32x4*)(smem + src.b + b_rd[sub] + f * T::FRAG);
 #pragma unroll
-      for (int f = 0; f < T::FM; ++f) yf[buf][f] = *(const u32x4*)(base + a_rd[sub] + f * 2048);
+      for (int f = 0; f < T::FM; ++f) yf[buf][f] = *(const u32x4*)(smem + src.a + a_rd[sub] + f * T::FRAG);
     };
 
     // Accumulators. The first K-tile is peeled: its first MFMA of every chain takes a zero
@@ -160,51 +180,64 @@ __global__ void __launch_bounds__(WM* WN * 64, 1) gemm_dma_kernel(GemmArgs args)
     };
     auto no_load = [](int) {};
 
-    // One K-tile: k-steps 0 .. NSUB-1 of ring slot `slot`. Before the last k-step of every tile
-    // but the last (kHandover, a compile-time flag so that the K-loop body is one straight-line
-    // block whose accumulators never meet at a join): wait for tile k+1, sync, then, threaded
-    // through the MFMAs, read tile k+1's first fragments and refill `slot` with tile k+S.
-    // With two stages the whole refill goes into the hand-over k-step (LW1 = LW). With three or
-    // more it is split in half so the loads spread over a whole K-tile: the first half in the
-    // hand-over k-step, the second in k-step 0 of the next tile (kDefer). The slot stays free
-    // from this hand-over's barrier to the next one, and by the next hand-over every load of
-    // tile k+S has been issued, so the vmcnt thresholds are unchanged.
-    // kFirst: the first tile, whose MFMA chains start from zero.
-    constexpr int LW1 = S > 2 ? T::LW / 2 : (S == 2 ? T::LW : 0);
-    auto k_tile = [&](int k, int slot, auto first_c, auto handover_c) {
+    // One K-tile: k-steps 0 .. NSUB-1 of the tile at ring position `pos`. Before the last k-step of
+    // every tile but the last (kHandover, a compile-time flag so that the K-loop body is one
+    // straight-line block whose accumulators never meet at a join): wait for tile k+1, sync, then,
+    // threaded through the MFMAs, read tile k+1's first fragments and refill the freed slots.
+    // Plain ring: tile k+S goes into tile k's stage. With two stages, or one k-step per K-tile,
+    // the whole refill goes into the hand-over k-step (LW1 = LW). Otherwise it is split in half so
+    // the loads spread over a whole K-tile: the first half in the hand-over k-step, the second in
+    // k-step 0 of the next tile (kDefer). The stage stays free from this hand-over's barrier to the
+    // next one, and by the next hand-over every load of tile k+S has been issued, so the vmcnt
+    // thresholds are unchanged.
+    // Split ring: tile k's two slots free up at its hand-over; the hand-over k-step loads tile
+    // k+2's B tile into tile k's A slot, and k-step 0 of tile k+1 loads tile k+3's A tile into tile
+    // k's B slot. Every k-step then issues one operand tile's loads. At a hand-over, tile k+1 must
+    // have landed and only tile k+2's A tile may still be in flight: vmcnt(LA).
+    // kFirst: the first tile, whose MFMA chains start from zero. b0_c: the fragment buffer the
+    // tile's k-step 0 uses (the k-step parity; it alternates per tile when a tile is one k-step).
+    constexpr int LW1 = T::SPLIT ? T::LB : (S > 2 && T::NSUB > 1 ? T::LW / 2 : (S >= 2 ? T::LW : 0));
+    constexpr int LWD = T::SPLIT ? T::LA : T::LW - LW1;  // deferred loads, in k-step 0 of the next tile
+    auto k_tile = [&](int k, int pos, auto first_c, auto handover_c, auto b0_c) {
       constexpr bool kFirst = decltype(first_c)::value;
       constexpr bool kHandover = decltype(handover_c)::value;
-      constexpr bool kDefer = !kFirst && S > 2;
-      const int next_slot = slot + 1 == S ? 0 : slot + 1;
-      const int prev_slot = slot == 0 ? S - 1 : slot - 1;
+      constexpr bool kDefer = !kFirst && (T::SPLIT || S > 2) && T::NSUB > 1;
+      const Regions cur = regions(pos), nxt = regions(pos_next(pos)), prv = regions(pos_prev(pos));
       static_for<T::NSUB>([&](auto sub_c) {
         constexpr int sub = decltype(sub_c)::value;
-        constexpr int buf = sub & 1;
+        constexpr int buf = (decltype(b0_c)::value + sub) & 1;
         auto zero_c = std::integral_constant<bool, kFirst && (sub == 0)>{};
         auto nr_c = std::integral_constant<int, T::FN + T::FM>{};
-        // second half of the refill started at the previous hand-over: tile k-1+S into prev_slot
-        auto nd_def = std::integral_constant<int, (kDefer && sub == 0) ? T::LW - LW1 : 0>{};
-        auto dm_def = [&](int d) { dma_one(prev_slot, k - 1 + S, LW1 + d); };
+        // second half of the refill started at the previous hand-over
+        auto nd_def = std::integral_constant<int, (kDefer && sub == 0) ? LWD : 0>{};
+        auto dm_def = [&](int d) {
+          if constexpr (T::SPLIT) dma_one(Regions{prv.b, prv.b}, k + 2, d);  // A of tile (k-1)+3
+          else dma_one(prv, k - 1 + S, LW1 + d);
+        };
         if constexpr (sub + 1 < T::NSUB) {
-          kstep(buf, zero_c, nr_c, nd_def, [&](int r) { read_frag(slot, sub + 1, buf ^ 1, r); }, dm_def);
+          kstep(buf, zero_c, nr_c, nd_def, [&](int r) { read_frag(cur, sub + 1, buf ^ 1, r); }, dm_def);
         } else if constexpr (kHandover) {
-          wait_lgkmcnt0();  // this wave's reads of `slot` are done
+          wait_lgkmcnt0();  // this wave's reads of tile k are done
           if constexpr (S == 1) {
             // serial: the only slot is refilled once everyone has read it, then waited on
             barrier_sync();
-            issue(0, k + 1);
+            issue(cur, k + 1);
             wait_vmcnt<0>();
             barrier_sync();
             kstep(buf, zero_c, nr_c, std::integral_constant<int, 0>{},
-                  [&](int r) { read_frag(0, 0, buf ^ 1, r); }, no_load);
+                  [&](int r) { read_frag(cur, 0, buf ^ 1, r); }, no_load);
           } else {
-            // every hand-over issued LW loads, so exactly tiles k+2 .. k+S-1 may still be in flight
-            wait_vmcnt<T::LW * (S - 2)>();
-            barrier_sync();  // tile k+1 visible to all waves; `slot` free in all waves
-            static_assert(T::NSUB >= 2, "the deferred half needs a k-step before the hand-over");
+            // plain ring: every hand-over issued LW loads, so exactly tiles k+2 .. k+S-1 may still be
+            // in flight; split ring: tile k+2's A tile
+            wait_vmcnt<T::SPLIT ? T::LA : T::LW * (S - 2)>();
+            barrier_sync();  // tile k+1 visible to all waves; tile k's slots free in all waves
+            static_assert(T::NSUB >= 2 || LW1 == T::LW, "the deferred half needs a k-step before the hand-over");
             kstep(buf, zero_c, nr_c, std::integral_constant<int, LW1>{},
-                  [&](int r) { read_frag(next_slot, 0, buf ^ 1, r); },
-                  [&](int d) { dma_one(slot, k + S, d); });
+                  [&](int r) { read_frag(nxt, 0, buf ^ 1, r); },
+                  [&](int d) {
+                    if constexpr (T::SPLIT) dma_one(Regions{cur.a, cur.a}, k + 2, T::LA + d);  // B of tile k+2
+                    else dma_one(cur, k + S, d);
+                  });
           }
         } else {
           kstep(buf, zero_c, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, no_load, no_load);
@@ -231,26 +264,57 @@ __global__ void __launch_bounds__(WM* WN * 64, 1) gemm_dma_kernel(GemmArgs args)
       barrier_sync();
     }
     first_tile = false;
-    // ---- prologue: fill the ring with tiles 0 .. min(S, KT) - 1 ----
+    // ---- prologue: fill the ring (tiles past K are zero-filling dummies) ----
+    if constexpr (T::SPLIT) {
+      // A0, B0, A1, B1, A2 into slots 0 .. 4
 #pragma unroll
-    for (int s = 0; s < S; ++s) issue(s, s);  // tiles past K are zero-filling dummies
-    wait_vmcnt<T::LW * (S - 1)>();            // this wave's part of tile 0 landed
-    barrier_sync();                           // ... and every wave's
-    read_frags(0, 0, 0);
+      for (int h = 0; h < S; ++h)
+#pragma unroll
+        for (int d = 0; d < (h % 2 ? T::LB : T::LA); ++d)
+          dma_one(Regions{h * T::SLOT, h * T::SLOT}, h / 2, (h % 2 ? T::LA : 0) + d);
+      wait_vmcnt<2 * T::LA + T::LB>();  // this wave's part of tile 0 landed
+    } else {
+#pragma unroll
+      for (int s = 0; s < S; ++s) issue(regions(s), s);
+      wait_vmcnt<T::LW * (S - 1)>();  // this wave's part of tile 0 landed
+    }
+    barrier_sync();  // ... and every wave's
+    read_frags(regions(0), 0, 0);
 
     // ---- steady state and drain: one barrier per K-tile; the last K-tile is peeled ----
     using t_ = std::true_type;
     using f_ = std::false_type;
+    using b0_ = std::integral_constant<int, 0>;
+    using b1_ = std::integral_constant<int, 1>;
     if (KT == 1) {
-      k_tile(0, 0, t_{}, f_{});
+      k_tile(0, 0, t_{}, f_{}, b0_{});
     } else {
-      k_tile(0, 0, t_{}, t_{});
-      int slot = S > 1 ? 1 : 0;
-      for (int k = 1; k < KT - 1; ++k) {
-        k_tile(k, slot, f_{}, t_{});
-        slot = slot + 1 == S ? 0 : slot + 1;
+      k_tile(0, 0, t_{}, t_{}, b0_{});
+      int slot = pos_next(0);
+      auto advance = [&]() { slot = pos_next(slot); };
+      if constexpr (T::NSUB % 2 == 0) {
+        for (int k = 1; k < KT - 1; ++k) {
+          k_tile(k, slot, f_{}, t_{}, b0_{});
+          advance();
+        }
+        k_tile(KT - 1, slot, f_{}, f_{}, b0_{});
+      } else {
+        // one k-step per K-tile: tile k uses fragment buffer k mod 2, so tiles go in pairs
+        int k = 1;
+        for (; k + 1 < KT - 1; k += 2) {
+          k_tile(k, slot, f_{}, t_{}, b1_{});
+          advance();
+          k_tile(k + 1, slot, f_{}, t_{}, b0_{});
+          advance();
+        }
+        if (k < KT - 1) {
+          k_tile(k, slot, f_{}, t_{}, b1_{});
+          advance();
+          ++k;
+        }
+        if (k & 1) k_tile(k, slot, f_{}, f_{}, b1_{});
+        else k_tile(k, slot, f_{}, f_{}, b0_{});
       }
-      k_tile(KT - 1, slot, f_{}, f_{});
     }
 
     // ---- epilogue: fp32 -> output type, 8 consecutive columns per lane ----
@@ -296,10 +360,9 @@ static KernelEntry make_entry() {
 
 const KernelEntry* dma_kernel_table(int* count) {
   static const KernelEntry table[] = {
-      make_entry<256, 256, 64, 2, 2, 4>(),
-      make_entry<256, 256, 64, 2, 4, 2>(),
-      make_entry<256, 256, 64, 1, 2, 4>(),
       make_entry<256, 256, 64, 2, 2, 2>(),
+      make_entry<256, 256, 64, 5, 2, 2>(),
+      make_entry<256, 256, 32, 4, 2, 2>(),
       make_entry<256, 256, 64, 1, 2, 2>(),
       make_entry<256, 128, 64, 3, 2, 2>(),
       make_entry<256, 128, 64, 2, 2, 2>(),

@@ -1,0 +1,262 @@
+// Software-pipelined, persistent, tiled GEMM  C = A·Bᵀ  for gfx950: the two-wave-group
+// ("ping-pong") form of the mainloop.
+//
+// The method is the one of spt_gemm.hip ("GEMM II — pipelining with TMA", Steps 4–6; "Multi-Stage
+// Software Pipelining", Prefill / Main loop): a ring of LDS stages filled ahead of the math by
+// direct global->LDS loads, a persistent pool of workgroups over a grouped raster. What changes
+// is who issues what, which is the step "Multi-Stage Software Pipelining" (What's Next) names
+// after the multi-stage ring: separate the loading role from the computing role.
+//
+// On gfx950 a wave issues at most one instruction per issue cycle, so with one wave per SIMD
+// every load and LDS read takes an issue slot from the MFMA stream. Here a workgroup has eight
+// waves, two per SIMD, in two groups of four (G0 = waves 0-3, G1 = waves 4-7; wave w runs on SIMD
+// w mod 4, so each SIMD holds one wave of each group). Time is cut into phases separated by
+// workgroup barriers; in every phase one group runs a block of MFMAs (a compute phase) while the
+// other group issues its LDS fragment reads and, for G0, the DMA loads of the next K-tile (a
+// memory phase). The two groups are one phase apart, so each SIMD's matrix core is fed by one
+// wave while its partner's memory instructions issue beside it.
+//
+// Tile 256x256, K-tile 64. G0 computes output rows [0, 128) of the tile and G1 rows [128, 256);
+// inside a group the four waves form a 2x2 grid of 64x128 wave tiles (128 fp32 accumulators per
+// lane). With KT K-tiles, K-tile u is read in phases 2u (G0) and 2u+1 (G1) and computed in phases
+// 2u+1 (G0) and 2u+2 (G1); G0 stores its half of the tile in phase 2KT, beside G1's last MFMAs,
+// and G1 stores after the last barrier. Both groups pass 2·KT + 2 barriers per output tile.
+//
+// Ring, S = 2: two 64 KiB stages. In phase 2u G0 loads all of K-tile u+1 into the other stage and
+// waits for it at the end of phase 2u+1: loads are issued in bursts, every other phase.
+// Ring, S = 5 (split): five 32 KiB operand slots; K-tile u's A tile sits in slot 2u mod 5 and its
+// B tile in slot 2u+1 mod 5. Every memory phase issues one operand tile: G0 loads B(u+1) in phase
+// 2u (into the slot A(u-1) left) and waits for it at the end of phase 2u+1; G1 loads A(u+2) in
+// phase 2u+1 (into the slot B(u-1) left) and waits for it two phases later, at the end of phase
+// 2u+3, with A(u+3) possibly still in flight. The prologue loads A(0), B(0) and A(1). Each load has
+// two (B) or three (A) phases to land, and the CU's fill path is busy in every phase.
+#include "spt_device.h"
+#include "spt_kernels.h"
+
+namespace spt {
+
+template <int S, typename TIn, int OUT>
+__global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmArgs args) {
+  constexpr int BM = 256, BN = 256, BK = 64;
+  constexpr bool SPLIT = S == 5;
+  constexpr int TM = 64, TN = 128;                   // wave tile
+  constexpr int FM = TM / 16, FN = TN / 16;          // 4 A fragments, 8 B fragments per k-step
+  constexpr int NSUB = BK / 32;                      // 2 k-steps per K-tile
+  constexpr int FRAG = 16 * 128;                     // bytes between 16-row fragments
+  constexpr int A_BYTES = BM * BK * 2, STAGE = (BM + BN) * BK * 2;
+  constexpr int LDS = SPLIT ? S * A_BYTES : S * STAGE;
+  constexpr int LA = A_BYTES / 1024 / 4, LB = LA;    // DMA instructions per wave for one operand tile
+  static_assert(S == 2 || S == 5, "two 64 KiB stages or five 32 KiB operand slots");
+  static_assert(LDS <= 160 * 1024, "LDS ring fits the 160 KiB of a CU");
+  __shared__ __attribute__((aligned(1024))) char smem[LDS];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int grp = wave >> 2, v = wave & 3;
+  const int wm = v >> 1, wn = v & 1;
+  const int M = args.M, N = args.N, K = args.K;
+  const int KT = (K + BK - 1) / BK;
+
+  // DMA. Wave v's instruction j of an operand tile fills LDS rows 8q .. 8q+7 (q = LA*v + j) of the
+  // tile; lane l lands at row 8q + l/8, physical chunk l%8, which holds logical chunk (l%8) XOR
+  // swz(l/8) (the swizzle has period 8 in the row, so it depends on the lane alone). The row
+  // splits into a wave-uniform part 8q and a lane part l/8; B rows are staged permuted, and
+  // b_row_perm splits the same way (it permutes within aligned 32-row groups).
+  const int lrow = lane >> 3;
+  const int lane_kc = 8 * ((lane & 7) ^ swz(lrow));
+  const int a_lrow = lrow, b_lrow = b_row_perm(lrow);
+  auto a_urow = [&](int j) { return 8 * (LA * v + j); };
+  auto b_urow = [&](int j) { return b_row_perm(8 * (LB * v + j)); };
+  // fragment read offsets inside an operand tile, k-step s (fragment f adds 16 rows)
+  int a_rd[NSUB], b_rd[NSUB];
+#pragma unroll
+  for (int s = 0; s < NSUB; ++s) {
+    a_rd[s] = lds_chunk_offset(BM, 128 * grp + TM * wm + (lane & 15), 4 * s + (lane >> 4));
+    b_rd[s] = lds_chunk_offset(BN, TN * wn + (lane & 15), 4 * s + (lane >> 4));
+  }
+  // LDS byte offsets of K-tile u's A and B tiles
+  auto a_at = [&](int u) { return SPLIT ? (2 * u) % S * A_BYTES : u % S * STAGE; };
+  auto b_at = [&](int u) { return SPLIT ? (2 * u + 1) % S * A_BYTES : u % S * STAGE + A_BYTES; };
+
+  const int u0 = xcd_remap(blockIdx.x, args.grid);
+  for (int t = u0; t < args.num_tiles; t += args.grid) {
+    int tm, tn;
+    grouped_raster(t, args.tiles_m, args.tiles_n, args.group_m, tm, tn);
+    const int row0 = tm * BM, col0 = tn * BN;
+    const int rows_left = M - row0, cols_left = N - col0;
+    const int es = OUT == 2 ? 4 : 2;
+    const __amdgpu_buffer_rsrc_t rc =
+        make_rsrc((char*)args.C + (size_t)row0 * args.ldc * es, ((uint64_t)(rows_left - 1) * args.ldc + N) * es);
+    const int m_base = 128 * grp + TM * wm;  // this wave's first output row inside the tile
+
+    if (KT == 0) {  // empty sum: C = 0 (no barriers: every wave takes this branch)
+      const float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      for (int pu = 0; pu < FN / 2; ++pu)
+        for (int j = 0; j < FM; ++j)
+          store8<OUT, true>(z, rc, m_base + 16 * j + (lane & 15), rows_left,
+                            col0 + TN * wn + 32 * pu + 8 * (lane >> 4), N, args.ldc);
+      continue;
+    }
+
+    u32x4 xf[NSUB][FN], yf[NSUB][FM];  // the K-tile's fragments: B side (x), A side (y)
+    f32x4 acc[FN][FM];
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc((const char*)args.A + (size_t)row0 * args.lda * 2,
+                                                ((uint64_t)(rows_left - 1) * args.lda + K) * 2);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc((const char*)args.B + (size_t)col0 * args.ldb * 2,
+                                                ((uint64_t)(cols_left - 1) * args.ldb + K) * 2);
+    // This wave's share of K-tile kt's A (or B) tile into the LDS tile at byte offset `dst`. The
+    // lane's offset is its row times ld plus its chunk; a row past the matrix edge then lies at or
+    // beyond the descriptor's num_records and reads zero. A chunk at or past K is moved beyond
+    // num_records explicitly (one select per call); the K offset rides in the scalar offset.
+    auto issue_a = [&](int dst, int kt) {
+      const int k0 = kt * BK;
+      const unsigned a0 = lane_kc < K - k0 ? (unsigned)(a_lrow * args.lda + lane_kc) * 2u : kOOB;
+      char* sa = smem + dst + LA * v * 1024;
+#pragma unroll
+      for (int j = 0; j < LA; ++j)
+        dma16_unseen(ra, sa + j * 1024, add_in_place(a0, (unsigned)(a_urow(j) * args.lda) * 2u), 2u * k0);
+    };
+    auto issue_b = [&](int dst, int kt) {
+      const int k0 = kt * BK;
+      const unsigned b0 = lane_kc < K - k0 ? (unsigned)(b_lrow * args.ldb + lane_kc) * 2u : kOOB;
+      char* sb = smem + dst + LB * v * 1024;
+#pragma unroll
+      for (int j = 0; j < LB; ++j)
+        dma16_unseen(rb, sb + j * 1024, add_in_place(b0, (unsigned)(b_urow(j) * args.ldb) * 2u), 2u * k0);
+    };
+    auto read_frags = [&](int u) {
+      const char* pa = smem + opaque_s32(a_at(u));
+      const char* pb = smem + opaque_s32(b_at(u));
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s) {
+#pragma unroll
+        for (int f = 0; f < FN; ++f) xf[s][f] = *(const u32x4*)(pb + b_rd[s] + f * FRAG);
+#pragma unroll
+        for (int f = 0; f < FM; ++f) yf[s][f] = *(const u32x4*)(pa + a_rd[s] + f * FRAG);
+      }
+      wait_lgkmcnt0();
+    };
+    // the MFMAs of one K-tile; kFirst starts every chain from zero (accumulate = (k != 0))
+    auto compute = [&](auto first_c) {
+      constexpr bool kFirst = decltype(first_c)::value;
+      __builtin_amdgcn_s_setprio(1);
+      static_for<NSUB>([&](auto s_c) {
+        constexpr int s = decltype(s_c)::value;
+        static_for<FN * FM>([&](auto m_c) {
+          constexpr int m = decltype(m_c)::value, i = m / FM, j = m % FM;
+          acc[i][j] = mfma16<TIn>(xf[s][i], yf[s][j], (kFirst && s == 0) ? zero4 : acc[i][j]);
+        });
+      });
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(0);
+    };
+    // The lane index is re-read through an opaque move, so the epilogue's address arithmetic stays
+    // here instead of being hoisted into registers held across the K-loop.
+    auto epilogue = [&](auto edge_c) {
+      constexpr bool kEdge = decltype(edge_c)::value;
+      const int ln = (int)opaque_u32((unsigned)lane);
+      const int m_lane = m_base + (ln & 15), n_lane = col0 + TN * wn + 8 * (ln >> 4);
+      const unsigned voff = (unsigned)(m_lane * args.ldc + n_lane) * (unsigned)es;
+#pragma unroll
+      for (int pu = 0; pu < FN / 2; ++pu) {
+#pragma unroll
+        for (int j = 0; j < FM; ++j) {
+          float vv[8];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            vv[e] = acc[2 * pu][j][e];
+            vv[4 + e] = acc[2 * pu + 1][j][e];
+          }
+          if constexpr (kEdge)
+            store8<OUT, true>(vv, rc, m_lane + 16 * j, rows_left, n_lane + 32 * pu, N, args.ldc);
+          else
+            store8_at<OUT>(vv, rc, voff, (unsigned)((16 * j * args.ldc + 32 * pu) * es));
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    };
+    const bool full_tile = rows_left >= BM && cols_left >= BN;
+
+    if (grp == 0) {
+      // ------------------------------------------------------------------------- G0
+      issue_a(a_at(0), 0);
+      issue_b(b_at(0), 0);
+      if (SPLIT && KT > 1) {
+        issue_a(a_at(1), 1);
+        wait_vmcnt<LA>();  // K-tile 0 landed; A(1) may be in flight
+      } else {
+        wait_vmcnt<0>();
+      }
+      barrier_sync();  // K-tile 0 visible
+      auto step = [&](int u, auto first_c) {
+        // phase 2u: memory
+        if (u + 1 < KT) {
+          if constexpr (SPLIT) issue_b(b_at(u + 1), u + 1);
+          else {
+            issue_a(a_at(u + 1), u + 1);
+            issue_b(b_at(u + 1), u + 1);
+          }
+        }
+        read_frags(u);
+        barrier_sync();
+        // phase 2u+1: compute K-tile u, then make sure this group's loads for K-tile u+1 landed
+        compute(first_c);
+        wait_vmcnt<0>();
+        barrier_sync();
+      };
+      step(0, std::true_type{});
+      for (int u = 1; u < KT; ++u) step(u, std::false_type{});
+      // phase 2KT: epilogue, beside G1's last compute phase
+      if (full_tile) epilogue(std::false_type{});
+      else epilogue(std::true_type{});
+      barrier_sync();
+    } else {
+      // ------------------------------------------------------------------------- G1
+      barrier_sync();  // K-tile 0 visible
+      barrier_sync();  // phase 0: idle
+      auto step = [&](int u, auto first_c) {
+        // phase 2u+1: memory
+        if (SPLIT && u + 2 < KT) issue_a(a_at(u + 2), u + 2);
+        read_frags(u);
+        if constexpr (SPLIT) {
+          // A(u+1), loaded two phases ago, must have landed; A(u+2) may still be in flight
+          if (u + 2 < KT) wait_vmcnt<LA>();
+          else wait_vmcnt<0>();
+        }
+        barrier_sync();
+        // phase 2u+2: compute
+        compute(first_c);
+        barrier_sync();
+      };
+      step(0, std::true_type{});
+      for (int u = 1; u < KT; ++u) step(u, std::false_type{});
+      // after the last barrier, beside G0's prologue of the next tile
+      if (full_tile) epilogue(std::false_type{});
+      else epilogue(std::true_type{});
+    }
+  }
+}
+
+template <int S>
+static KernelEntry make_pp_entry() {
+  KernelEntry k;
+  k.bm = 256; k.bn = 256; k.bk = 64; k.stages = S; k.waves = 8; k.load_path = 1;
+  k.lds_bytes = S == 5 ? 5 * 256 * 64 * 2 : S * (256 + 256) * 64 * 2;
+  k.fn[0][0] = (const void*)&gemm_pp_kernel<S, _Float16, 0>;
+  k.fn[0][1] = (const void*)&gemm_pp_kernel<S, _Float16, 1>;
+  k.fn[0][2] = (const void*)&gemm_pp_kernel<S, _Float16, 2>;
+  k.fn[1][0] = (const void*)&gemm_pp_kernel<S, __bf16, 0>;
+  k.fn[1][1] = (const void*)&gemm_pp_kernel<S, __bf16, 1>;
+  k.fn[1][2] = (const void*)&gemm_pp_kernel<S, __bf16, 2>;
+  return k;
+}
+
+const KernelEntry* pp_kernel_table(int* count) {
+  static const KernelEntry table[] = {make_pp_entry<5>(), make_pp_entry<2>()};
+  *count = (int)(sizeof(table) / sizeof(table[0]));
+  return table;
+}
+
+}  // namespace spt

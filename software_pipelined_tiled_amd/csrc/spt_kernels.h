@@ -11,5 +11,6 @@ struct KernelEntry {
 
 const KernelEntry* dma_kernel_table(int* count);
 const KernelEntry* reg_kernel_table(int* count);
+const KernelEntry* pp_kernel_table(int* count);  // two wave groups (waves = 8), DMA loads
 
 }  // namespace spt

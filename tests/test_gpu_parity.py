@@ -30,11 +30,19 @@ from gpu_helpers import check_full, check_sampled, run_gpu, sample_indices  # no
 DMA_CONFIGS = [(256, 256, 2), (256, 256, 1), (256, 128, 3), (256, 128, 2), (256, 128, 1), (128, 128, 4),
                (128, 128, 3), (128, 128, 2), (128, 128, 1), (64, 64, 4), (64, 64, 2)]
 REG_CONFIGS = [(128, 128, 2), (64, 64, 2)]
+# (bk, stages, waves) of the 256x256 configurations with their own ring shape: the split ring of
+# five operand slots, 32-deep K-tiles with four stages, and the two-wave-group kernel (split ring,
+# and two stages)
+RING_CONFIGS = [(64, 5, 4), (32, 4, 4), (64, 5, 8), (64, 2, 8)]
 
 
-def cfg(bm, bn, s, path=spt.GEMM_LOAD_DMA, persistent=1, group_m=8, grid=0):
-    return dict(bm=bm, bn=bn, bk=64, stages=s, waves=4, mfma=16, persistent=persistent, group_m=group_m,
+def cfg(bm, bn, s, path=spt.GEMM_LOAD_DMA, persistent=1, group_m=8, grid=0, bk=64, waves=4):
+    return dict(bm=bm, bn=bn, bk=bk, stages=s, waves=waves, mfma=16, persistent=persistent, group_m=group_m,
                 load_path=path, grid=grid, lds_bytes=0)
+
+
+def ring_cfg(bk, s, waves, **kw):
+    return cfg(256, 256, s, bk=bk, waves=waves, **kw)
 
 
 def ints(rows, cols, dtype, seed, ld=None):
@@ -58,6 +66,31 @@ def test_dma_configs_bit_exact(bm, bn, s, persistent):
         check_full(a, b, K, in_dt, si.F32, c, N, exact=True)
 
 
+@pytest.mark.parametrize("bk,s,waves", RING_CONFIGS)
+@pytest.mark.parametrize("persistent", [1, 0])
+def test_ring_configs_bit_exact(bk, s, waves, persistent):
+    # 2 x 2 tiles with ragged edges; K spans several K-tiles plus a partial one
+    M, N, K = 256 + 131, 512 - 37, 7 * 64 + 24
+    for in_dt in (si.F16, si.BF16):
+        a = ints(M, K, in_dt, 500 + bk + s + waves)
+        b = ints(N, K, in_dt, 600 + bk + s + waves)
+        c, desc = run_gpu(a, b, K, in_dt, si.F32,
+                          config=ring_cfg(bk, s, waves, persistent=persistent, grid=3 if persistent else 0))
+        assert (desc["bk"], desc["stages"], desc["waves"]) == (bk, s, waves)
+        check_full(a, b, K, in_dt, si.F32, c, N, exact=True)
+
+
+@pytest.mark.parametrize("K", [8, 64, 72, 128, 136, 192, 256, 320, 648])
+@pytest.mark.parametrize("bk,s,waves", RING_CONFIGS)
+def test_ring_configs_k_around_depth(K, bk, s, waves):
+    # fewer K-tiles than ring slots, about as many, and more; K tails of 8 .. 56 elements
+    M, N = 300, 260
+    a = ints(M, K, si.BF16, 3 * K + s)
+    b = ints(N, K, si.BF16, 3 * K + s + 1)
+    c, _ = run_gpu(a, b, K, si.BF16, si.F32, config=ring_cfg(bk, s, waves, grid=2))
+    check_full(a, b, K, si.BF16, si.F32, c, N, exact=True)
+
+
 @pytest.mark.parametrize("bm,bn,s", REG_CONFIGS)
 def test_reg_configs_bit_exact(bm, bn, s):
     M, N, K = 2 * bm + 7, bn + 9, 3 * 64 + 13  # K not a multiple of 8: element-masked tail
@@ -77,7 +110,8 @@ def test_output_dtypes_bit_exact(in_dt, out_dt):
     M, N, K = 300, 264, 320
     a = ints(M, K, in_dt, 7)
     b = ints(N, K, in_dt, 8)
-    for c_cfg in (cfg(256, 256, 2), cfg(128, 128, 4), cfg(128, 128, 2, path=spt.GEMM_LOAD_REG)):
+    for c_cfg in (cfg(256, 256, 2), cfg(128, 128, 4), cfg(128, 128, 2, path=spt.GEMM_LOAD_REG),
+                  ring_cfg(64, 5, 8), ring_cfg(64, 5, 4)):
         c, _ = run_gpu(a, b, K, in_dt, out_dt, config=c_cfg)
         check_full(a, b, K, in_dt, out_dt, c, N, exact=True)
 
@@ -173,4 +207,7 @@ def test_workload_c1_small_full_through_each_dma_config():
     m, n, k, a, b, i_dt, o_dt = si.workload_operands("c1_256_f16_f32")
     for bm, bn, s in DMA_CONFIGS:
         c, _ = run_gpu(a, b, k, i_dt, o_dt, config=cfg(bm, bn, s))
+        check_full(a, b, k, i_dt, o_dt, c, n)
+    for bk, s, waves in RING_CONFIGS:
+        c, _ = run_gpu(a, b, k, i_dt, o_dt, config=ring_cfg(bk, s, waves))
         check_full(a, b, k, i_dt, o_dt, c, n)

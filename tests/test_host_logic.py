@@ -80,11 +80,19 @@ WORKLOAD_SHAPES = {
 }
 
 
+def ring_bytes(c):
+    """LDS of a configuration's ring: S stages of an A and a B K-tile, or, for the split ring (bk
+    64, five slots, square tile), five operand slots of one K-tile each."""
+    if c["load_path"] == spt.GEMM_LOAD_DMA and c["bk"] == 64 and c["stages"] == 5 and c["bm"] == c["bn"]:
+        return 5 * c["bm"] * c["bk"] * 2
+    return c["stages"] * (c["bm"] + c["bn"]) * c["bk"] * 2
+
+
 @pytest.mark.parametrize("name", sorted(WORKLOAD_SHAPES))
 def test_config_choice(name):
     M, N, K, i, o = WORKLOAD_SHAPES[name]
     c = spt.gemm_select_config(M, N, K, i, i, o, K, K, N, 256, 160 * 1024)
-    assert c["lds_bytes"] == c["stages"] * (c["bm"] + c["bn"]) * c["bk"] * 2 <= 160 * 1024
+    assert c["lds_bytes"] == ring_bytes(c) <= 160 * 1024
     tiles = math.ceil(M / c["bm"]) * math.ceil(N / c["bn"])
     assert 1 <= c["grid"] <= min(tiles, 512)
     if K % 8 == 0:
@@ -92,7 +100,9 @@ def test_config_choice(name):
     else:
         assert c["load_path"] == spt.GEMM_LOAD_REG  # lda = 3071: rows are only 2-byte aligned
     if name in ("c2", "c3", "c4"):
-        assert (c["bm"], c["bn"], c["stages"]) == (256, 256, 2) and tiles >= 256
+        # the two-wave-group kernel with the split ring
+        assert (c["bm"], c["bn"], c["bk"], c["stages"], c["waves"]) == (256, 256, 64, 5, 8) and tiles >= 256
+        assert c["lds_bytes"] == 160 * 1024
     if name == "c5c":
         assert tiles >= 256  # the tile menu fills every CU
 
@@ -202,6 +212,8 @@ def test_lds_swizzle_spreads_every_eight_row_column():
 
 DMA_TABLE = [(256, 256, 2), (256, 256, 1), (256, 128, 3), (256, 128, 2), (256, 128, 1), (128, 128, 4),
              (128, 128, 3), (128, 128, 2), (128, 128, 1), (64, 64, 4), (64, 64, 2)]
+# (bm, bn, bk, stages, waves) of the configurations with their own ring shape
+RING_TABLE = [(256, 256, 64, 5, 4), (256, 256, 32, 4, 4), (256, 256, 64, 5, 8), (256, 256, 64, 2, 8)]
 
 
 def stage_bytes(bm, bn, bk, elem=2):
@@ -224,6 +236,23 @@ def test_stage_accounting_of_every_dma_config(bm, bn, s):
     # vmcnt thresholds used by the ring: lw * (S-2) in steady state, up to lw * (S-1) after the prologue
     assert lw * max(s - 1, 1) < 64
     assert s * total <= 160 * 1024
+
+
+@pytest.mark.parametrize("bm,bn,bk,s,waves", RING_TABLE)
+def test_stage_accounting_of_ring_configs(bm, bn, bk, s, waves):
+    cfg = dict(bm=bm, bn=bn, bk=bk, stages=s, waves=waves, load_path=spt.GEMM_LOAD_DMA)
+    assert ring_bytes(cfg) <= 160 * 1024
+    if waves == 8:
+        # one group of four waves loads an operand tile: 1 KiB per instruction
+        la = bm * bk * 2 // (1024 * 4)
+        assert la == 8 and (bm * bk * 2) % (1024 * 4) == 0
+        assert la * 2 < 64  # the largest threshold: a stage, or an operand tile plus one in flight
+    elif s == 5 and bk == 64:
+        la, lb = bm * bk * 2 // (1024 * waves), bn * bk * 2 // (1024 * waves)
+        assert 2 * la + lb < 64  # prologue threshold of the split ring
+    else:
+        lw = stage_bytes(bm, bn, bk) // (1024 * waves)
+        assert lw * (s - 1) < 64
 
 
 # ------------------------------------------------------------------------------ ring protocol replay
@@ -294,3 +323,148 @@ def test_ring_replay_catches_planted_mistakes(S):
     with pytest.raises(AssertionError, match="refilled"):
         for KT in range(1, 2 * S + 3):
             replay_ring(KT, S, LW=4, refill_before_barrier=True)
+
+
+# The split ring (five operand slots of one K-tile each): K-tile k's A tile is operand tile 2k, its B
+# tile 2k+1, and operand tile h sits in slot h mod 5. The prologue loads operand tiles 0 .. 4; k-step
+# 0 of tile k (k >= 1) loads A(k+2); at tile k's hand-over the wave waits until at most LA loads are
+# outstanding, syncs, and loads B(k+2) during the hand-over k-step. Tiles past the end are dummies.
+def replay_split_ring(KT, LA, LB, wait_slack=0, early_b=False):
+    issued = []        # operand tile of each load, in order
+    slot_of = {}       # slot -> operand tile it holds
+    read = set()       # K-tiles whose fragment reads completed everywhere (lgkmcnt(0) + barrier)
+    landed_upto = -1
+
+    def load(h):
+        slot = h % 5
+        prev = slot_of.get(slot)
+        if prev is not None and prev // 2 < KT:
+            assert prev // 2 in read, f"slot {slot} refilled with operand tile {h} before K-tile {prev // 2} was read"
+        slot_of[slot] = h
+        issued.extend([h] * (LA if h % 2 == 0 else LB))
+
+    def wait_vm(n):
+        nonlocal landed_upto
+        landed_upto = max(landed_upto, len(issued) - 1 - n)
+
+    def landed(k):
+        idx = [i for i, h in enumerate(issued) if h in (2 * k, 2 * k + 1)]
+        return idx and max(idx) <= landed_upto and slot_of[(2 * k) % 5] == 2 * k and slot_of[(2 * k + 1) % 5] == 2 * k + 1
+
+    for h in range(5):
+        load(h)
+    wait_vm(2 * LA + LB)
+    assert landed(0), "K-tile 0 read before it landed"
+    for k in range(KT):
+        if k >= 1:
+            load(2 * (k + 2))                 # A(k+2), k-step 0
+        if early_b and k + 1 < KT:
+            load(2 * (k + 2) + 1)             # planted mistake: B(k+2) before the hand-over barrier
+        if k + 1 < KT:
+            read.add(k)                       # hand-over: every wave's reads of tile k are done
+            wait_vm(LA + wait_slack)
+            assert landed(k + 1), f"K-tile {k + 1} read before it landed (KT={KT})"
+            if not early_b:
+                load(2 * (k + 2) + 1)         # B(k+2), hand-over k-step
+        else:
+            read.add(k)
+
+
+def test_split_ring_replay():
+    for KT in range(1, 12):
+        replay_split_ring(KT, LA=8, LB=8)
+
+
+def test_split_ring_replay_catches_planted_mistakes():
+    with pytest.raises(AssertionError, match="before it landed"):
+        for KT in range(1, 12):
+            replay_split_ring(KT, LA=8, LB=8, wait_slack=1)
+    with pytest.raises(AssertionError, match="refilled"):
+        for KT in range(1, 12):
+            replay_split_ring(KT, LA=8, LB=8, early_b=True)
+
+
+# The two-wave-group schedule. Phases are separated by workgroup barriers; K-tile u is read by G0 in
+# phase 2u and by G1 in phase 2u+1. S = 2: G0 loads K-tile u+1 (both operand tiles) in phase 2u and
+# waits vmcnt(0) at the end of phase 2u+1. S = 5 (split): G0 loads B(u+1) in phase 2u and waits
+# vmcnt(0) at the end of phase 2u+1; G1 loads A(u+2) in phase 2u+1 and, at the end of that phase,
+# waits until at most LA of its loads are outstanding (none when it loaded nothing). The prologue
+# (G0) loads A(0), B(0) and, for S = 5, A(1), then waits for K-tile 0.
+def replay_two_groups(KT, S, LA, g1_slack=0, g0_late_wait=False):
+    loads = {0: [], 1: []}       # per group: operand tile of each load, in order
+    landed = {0: -1, 1: -1}
+    slot_of = {}
+    read_done = {}               # K-tile -> phase after which both groups finished reading it
+    n_slots = 5 if S == 5 else 2
+
+    def slot(h):
+        return h % 5 if S == 5 else (h // 2) % 2 * 2 + h % 2   # S = 2: stage (k mod 2), A or B half
+
+    def load(g, h, phase):
+        sl = slot(h)
+        prev = slot_of.get(sl)
+        if prev is not None:
+            assert read_done.get(prev // 2, 1 << 30) < phase, f"slot {sl} refilled in phase {phase} before K-tile {prev // 2} was read"
+        slot_of[sl] = h
+        loads[g].extend([h] * LA)
+
+    def wait(g, n):
+        landed[g] = max(landed[g], len(loads[g]) - 1 - n)
+
+    def is_landed(h):
+        for g in (0, 1):
+            idx = [i for i, x in enumerate(loads[g]) if x == h]
+            if idx:
+                return max(idx) <= landed[g] and slot_of[slot(h)] == h
+        return False
+
+    def check_read(u, phase):
+        for h in (2 * u, 2 * u + 1):
+            assert is_landed(h), f"operand tile {h} read in phase {phase} before it landed (KT={KT}, S={S})"
+
+    # prologue (G0)
+    load(0, 0, -1)
+    load(0, 1, -1)
+    if S == 5 and KT > 1:
+        load(0, 2, -1)
+        wait(0, LA)
+    else:
+        wait(0, 0)
+    for u in range(KT):
+        p0, p1 = 2 * u, 2 * u + 1
+        # phase 2u: G0 memory (loads, then reads K-tile u); G1 computes K-tile u-1
+        if u + 1 < KT:
+            if S == 5:
+                load(0, 2 * (u + 1) + 1, p0)
+            else:
+                load(0, 2 * (u + 1), p0)
+                load(0, 2 * (u + 1) + 1, p0)
+        check_read(u, p0)
+        # phase 2u+1: G0 computes K-tile u, then waits; G1 memory (loads, reads K-tile u, waits)
+        g1_loaded = False
+        if S == 5 and u + 2 < KT:
+            load(1, 2 * (u + 2), p1)
+            g1_loaded = True
+        check_read(u, p1)
+        read_done[u] = p1
+        if not g0_late_wait:
+            wait(0, 0)
+        if S == 5:
+            wait(1, (LA if g1_loaded else 0) + g1_slack)
+        # barrier at the end of phase 2u+1
+    return n_slots
+
+
+@pytest.mark.parametrize("S", [2, 5])
+def test_two_group_schedule_replay(S):
+    for KT in range(1, 12):
+        replay_two_groups(KT, S, LA=8)
+
+
+def test_two_group_replay_catches_planted_mistakes():
+    with pytest.raises(AssertionError, match="before it landed"):
+        for KT in range(1, 12):
+            replay_two_groups(KT, 5, LA=8, g1_slack=1)
+    with pytest.raises(AssertionError, match="before it landed"):
+        for KT in range(1, 12):
+            replay_two_groups(KT, 2, LA=8, g0_late_wait=True)
