@@ -7,6 +7,10 @@
 
 #include "spt_common.h"
 
+// Lambdas inside kernels are marked with this: an out-of-line call would pass the accumulator array
+// through scratch memory.
+#define SPT_INLINE __attribute__((always_inline))
+
 namespace spt {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -58,14 +62,18 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, unsig
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, voffset, soffset, 0, 0);
 }
 
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ unsigned lds_addr(const void* p) { return (unsigned)(uintptr_t)(const lds_void_t*)p; }
+
 // The same load issued through inline assembly (the LDS address travels in M0), so the compiler
 // does not see an LDS write: otherwise it guards every later LDS read that might alias the
 // destination with a wait for this load, which serialises fragment reads behind the loads in
 // flight. A kernel using it orders its LDS reads after its own loads explicitly (s_waitcnt vmcnt,
 // then s_barrier) before any wave reads a tile.
-__device__ __forceinline__ void dma16_unseen(__amdgpu_buffer_rsrc_t r, void* lds, unsigned voffset,
+// `lds` is the destination's LDS byte address (wave-uniform).
+__device__ __forceinline__ void dma16_unseen(__amdgpu_buffer_rsrc_t r, unsigned lds, unsigned voffset,
                                              unsigned soffset) {
-  const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(lds_void_t*)lds);
+  const unsigned m0 = __builtin_amdgcn_readfirstlane(lds);
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :
                : "s"(m0), "v"(voffset), "s"(r), "s"(soffset)

@@ -18,22 +18,35 @@
 //
 // Tile 256x256, K-tile 64. G0 computes output rows [0, 128) of the tile and G1 rows [128, 256);
 // inside a group the four waves form a 2x2 grid of 64x128 wave tiles (128 fp32 accumulators per
-// lane). With KT K-tiles, K-tile u is read in phases 2u (G0) and 2u+1 (G1) and computed in phases
-// 2u+1 (G0) and 2u+2 (G1); G0 stores its half of the tile in phase 2KT, beside G1's last MFMAs,
-// and G1 stores after the last barrier. Both groups pass 2·KT + 2 barriers per output tile.
+// lane).
 //
-// Ring, S = 2: two 64 KiB stages. In phase 2u G0 loads all of K-tile u+1 into the other stage and
-// waits for it at the end of phase 2u+1: loads are issued in bursts, every other phase.
-// Ring, S = 5 (split): five 32 KiB operand slots; K-tile u's A tile sits in slot 2u mod 5 and its
-// B tile in slot 2u+1 mod 5. Every memory phase issues one operand tile: G0 loads B(u+1) in phase
-// 2u (into the slot A(u-1) left) and waits for it at the end of phase 2u+1; G1 loads A(u+2) in
-// phase 2u+1 (into the slot B(u-1) left) and waits for it two phases later, at the end of phase
-// 2u+3, with A(u+3) possibly still in flight. The prologue loads A(0), B(0) and A(1). Each load has
-// two (B) or three (A) phases to land, and the CU's fill path is busy in every phase.
+// The phases run on without a break from one output tile to the next: number the K-tiles a
+// workgroup computes g = 0, 1, ..., G-1 across all its output tiles (KT per tile). K-tile g is read
+// in phases 2g (G0) and 2g+1 (G1) and computed in phases 2g+1 (G0) and 2g+2 (G1). Loads run ahead
+// into the next output tile the same way they run ahead inside one, so there is no prologue per
+// output tile (the pages' "overlap load k+1 with compute k and store k-1" carried across tiles).
+// A group stores a finished output tile in its next memory phase, before reading the next
+// fragments; after the last K-tile G0 stores in phase 2G, beside G1's last MFMAs, and G1 after
+// the last barrier. Both groups pass 2G + 2 barriers.
+//
+// Ring, S = 2: two 64 KiB stages (stage g mod 2). In phase 2g G0 loads all of K-tile g+1 and waits
+// for it at the end of phase 2g+1: loads are issued in bursts, every other phase.
+// Ring, S = 5 (split): five 32 KiB operand slots; K-tile g's A tile sits in slot 2g mod 5 and its
+// B tile in slot 2g+1 mod 5. Every memory phase issues one operand tile: G0 loads B(g+1) in phase
+// 2g (into the slot A(g-1) left) and waits for it at the end of phase 2g+1; G1 loads A(g+2) in
+// phase 2g+1 (into the slot B(g-1) left) and waits for it two phases later, with A(g+3) possibly
+// still in flight. The kernel starts by loading A(0), B(0) and A(1). Each load has two (B) or three
+// (A) phases to land, and the CU's fill path is busy in every phase.
 #include "spt_device.h"
 #include "spt_kernels.h"
 
 namespace spt {
+
+// One output tile of the raster (t >= num_tiles: past the end of this workgroup's list).
+struct PpTile {
+  int t;
+  int row0, col0, rows_left, cols_left;
+};
 
 template <int S, typename TIn, int OUT>
 __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmArgs args) {
@@ -49,6 +62,7 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmArgs args) {
   static_assert(S == 2 || S == 5, "two 64 KiB stages or five 32 KiB operand slots");
   static_assert(LDS <= 160 * 1024, "LDS ring fits the 160 KiB of a CU");
   __shared__ __attribute__((aligned(1024))) char smem[LDS];
+  const unsigned smem_base = lds_addr(smem);
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -56,6 +70,38 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmArgs args) {
   const int wm = v >> 1, wn = v & 1;
   const int M = args.M, N = args.N, K = args.K;
   const int KT = (K + BK - 1) / BK;
+  const int es = OUT == 2 ? 4 : 2;
+  const int m_base = 128 * grp + TM * wm;  // this wave's first output row inside a tile
+
+  auto tile_at = [&](int t) SPT_INLINE {
+    PpTile tl;
+    tl.t = t;
+    int tm = 0, tn = 0;
+    if (t < args.num_tiles) grouped_raster(t, args.tiles_m, args.tiles_n, args.group_m, tm, tn);
+    tl.row0 = tm * BM;
+    tl.col0 = tn * BN;
+    tl.rows_left = M - tl.row0;
+    tl.cols_left = N - tl.col0;
+    return tl;
+  };
+  auto c_rsrc = [&](const PpTile& tl) SPT_INLINE {
+    return make_rsrc((char*)args.C + (size_t)tl.row0 * args.ldc * es,
+                     ((uint64_t)(tl.rows_left - 1) * args.ldc + N) * es);
+  };
+
+  const int u0 = xcd_remap(blockIdx.x, args.grid);
+  if (KT == 0) {  // empty sum: C = 0 (no barriers: every wave takes this branch)
+    const float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int t = u0; t < args.num_tiles; t += args.grid) {
+      const PpTile tl = tile_at(t);
+      const __amdgpu_buffer_rsrc_t rc = c_rsrc(tl);
+      for (int pu = 0; pu < FN / 2; ++pu)
+        for (int j = 0; j < FM; ++j)
+          store8<OUT, true>(z, rc, m_base + 16 * j + (lane & 15), tl.rows_left,
+                            tl.col0 + TN * wn + 32 * pu + 8 * (lane >> 4), N, args.ldc);
+    }
+    return;
+  }
 
   // DMA. Wave v's instruction j of an operand tile fills LDS rows 8q .. 8q+7 (q = LA*v + j) of the
   // tile; lane l lands at row 8q + l/8, physical chunk l%8, which holds logical chunk (l%8) XOR
@@ -65,8 +111,8 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmArgs args) {
   const int lrow = lane >> 3;
   const int lane_kc = 8 * ((lane & 7) ^ swz(lrow));
   const int a_lrow = lrow, b_lrow = b_row_perm(lrow);
-  auto a_urow = [&](int j) { return 8 * (LA * v + j); };
-  auto b_urow = [&](int j) { return b_row_perm(8 * (LB * v + j)); };
+  auto a_urow = [&](int j) SPT_INLINE { return 8 * (LA * v + j); };
+  auto b_urow = [&](int j) SPT_INLINE { return b_row_perm(8 * (LB * v + j)); };
   // fragment read offsets inside an operand tile, k-step s (fragment f adds 16 rows)
   int a_rd[NSUB], b_rd[NSUB];
 #pragma unroll
@@ -74,168 +120,224 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmArgs args) {
     a_rd[s] = lds_chunk_offset(BM, 128 * grp + TM * wm + (lane & 15), 4 * s + (lane >> 4));
     b_rd[s] = lds_chunk_offset(BN, TN * wn + (lane & 15), 4 * s + (lane >> 4));
   }
-  // LDS byte offsets of K-tile u's A and B tiles
-  auto a_at = [&](int u) { return SPLIT ? (2 * u) % S * A_BYTES : u % S * STAGE; };
-  auto b_at = [&](int u) { return SPLIT ? (2 * u + 1) % S * A_BYTES : u % S * STAGE + A_BYTES; };
 
-  const int u0 = xcd_remap(blockIdx.x, args.grid);
-  for (int t = u0; t < args.num_tiles; t += args.grid) {
-    int tm, tn;
-    grouped_raster(t, args.tiles_m, args.tiles_n, args.group_m, tm, tn);
-    const int row0 = tm * BM, col0 = tn * BN;
-    const int rows_left = M - row0, cols_left = N - col0;
-    const int es = OUT == 2 ? 4 : 2;
-    const __amdgpu_buffer_rsrc_t rc =
-        make_rsrc((char*)args.C + (size_t)row0 * args.ldc * es, ((uint64_t)(rows_left - 1) * args.ldc + N) * es);
-    const int m_base = 128 * grp + TM * wm;  // this wave's first output row inside the tile
-
-    if (KT == 0) {  // empty sum: C = 0 (no barriers: every wave takes this branch)
-      const float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      for (int pu = 0; pu < FN / 2; ++pu)
-        for (int j = 0; j < FM; ++j)
-          store8<OUT, true>(z, rc, m_base + 16 * j + (lane & 15), rows_left,
-                            col0 + TN * wn + 32 * pu + 8 * (lane >> 4), N, args.ldc);
-      continue;
+  // A position in the K-tile stream: an output tile and a K-tile inside it. advance() moves to the
+  // next K-tile, into the next output tile after the last. (All of it is wave-uniform; the loads
+  // re-read it through readfirstlane so that it stays in scalar registers.)
+  struct Cursor {
+    PpTile tl;
+    int u;
+  };
+  auto cursor_at = [&](int t) SPT_INLINE {
+    Cursor c;
+    c.tl = tile_at(t);
+    c.u = 0;
+    return c;
+  };
+  auto advance = [&](Cursor& c) SPT_INLINE {
+    if (++c.u == KT) {
+      c.u = 0;
+      c.tl = tile_at(c.tl.t + args.grid);
     }
+  };
+  auto valid = [&](const Cursor& c) SPT_INLINE { return c.tl.t < args.num_tiles; };
 
-    u32x4 xf[NSUB][FN], yf[NSUB][FM];  // the K-tile's fragments: B side (x), A side (y)
-    f32x4 acc[FN][FM];
-    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-
+  // This wave's share of the A (or B) tile of the cursor's K-tile into the LDS tile at byte offset
+  // `dst`. The lane's offset is its row times ld plus its chunk; a row past the matrix edge then
+  // lies at or beyond the descriptor's num_records and reads zero. A chunk at or past K is moved
+  // beyond num_records explicitly (one select per call); the K offset rides in the scalar offset.
+  auto issue_a = [&](const Cursor& c, int dst) SPT_INLINE {
+    const int k0 = __builtin_amdgcn_readfirstlane(c.u) * BK;
+    const int row0 = __builtin_amdgcn_readfirstlane(c.tl.row0);
+    const int rows_left = __builtin_amdgcn_readfirstlane(c.tl.rows_left);
     const __amdgpu_buffer_rsrc_t ra = make_rsrc((const char*)args.A + (size_t)row0 * args.lda * 2,
                                                 ((uint64_t)(rows_left - 1) * args.lda + K) * 2);
+    const unsigned a0 = lane_kc < K - k0 ? (unsigned)(a_lrow * args.lda + lane_kc) * 2u : kOOB;
+    const unsigned sa = smem_base + (unsigned)__builtin_amdgcn_readfirstlane(dst) + LA * v * 1024;
+#pragma unroll
+    for (int j = 0; j < LA; ++j)
+      dma16_unseen(ra, sa + j * 1024, add_in_place(a0, (unsigned)(a_urow(j) * args.lda) * 2u), 2u * k0);
+  };
+  auto issue_b = [&](const Cursor& c, int dst) SPT_INLINE {
+    const int k0 = __builtin_amdgcn_readfirstlane(c.u) * BK;
+    const int col0 = __builtin_amdgcn_readfirstlane(c.tl.col0);
+    const int cols_left = __builtin_amdgcn_readfirstlane(c.tl.cols_left);
     const __amdgpu_buffer_rsrc_t rb = make_rsrc((const char*)args.B + (size_t)col0 * args.ldb * 2,
                                                 ((uint64_t)(cols_left - 1) * args.ldb + K) * 2);
-    // This wave's share of K-tile kt's A (or B) tile into the LDS tile at byte offset `dst`. The
-    // lane's offset is its row times ld plus its chunk; a row past the matrix edge then lies at or
-    // beyond the descriptor's num_records and reads zero. A chunk at or past K is moved beyond
-    // num_records explicitly (one select per call); the K offset rides in the scalar offset.
-    auto issue_a = [&](int dst, int kt) {
-      const int k0 = kt * BK;
-      const unsigned a0 = lane_kc < K - k0 ? (unsigned)(a_lrow * args.lda + lane_kc) * 2u : kOOB;
-      char* sa = smem + dst + LA * v * 1024;
+    const unsigned b0 = lane_kc < K - k0 ? (unsigned)(b_lrow * args.ldb + lane_kc) * 2u : kOOB;
+    const unsigned sb = smem_base + (unsigned)__builtin_amdgcn_readfirstlane(dst) + LB * v * 1024;
 #pragma unroll
-      for (int j = 0; j < LA; ++j)
-        dma16_unseen(ra, sa + j * 1024, add_in_place(a0, (unsigned)(a_urow(j) * args.lda) * 2u), 2u * k0);
-    };
-    auto issue_b = [&](int dst, int kt) {
-      const int k0 = kt * BK;
-      const unsigned b0 = lane_kc < K - k0 ? (unsigned)(b_lrow * args.ldb + lane_kc) * 2u : kOOB;
-      char* sb = smem + dst + LB * v * 1024;
-#pragma unroll
-      for (int j = 0; j < LB; ++j)
-        dma16_unseen(rb, sb + j * 1024, add_in_place(b0, (unsigned)(b_urow(j) * args.ldb) * 2u), 2u * k0);
-    };
-    auto read_frags = [&](int u) {
-      const char* pa = smem + opaque_s32(a_at(u));
-      const char* pb = smem + opaque_s32(b_at(u));
-#pragma unroll
-      for (int s = 0; s < NSUB; ++s) {
-#pragma unroll
-        for (int f = 0; f < FN; ++f) xf[s][f] = *(const u32x4*)(pb + b_rd[s] + f * FRAG);
-#pragma unroll
-        for (int f = 0; f < FM; ++f) yf[s][f] = *(const u32x4*)(pa + a_rd[s] + f * FRAG);
-      }
-      wait_lgkmcnt0();
-    };
-    // the MFMAs of one K-tile; kFirst starts every chain from zero (accumulate = (k != 0))
-    auto compute = [&](auto first_c) {
-      constexpr bool kFirst = decltype(first_c)::value;
-      __builtin_amdgcn_s_setprio(1);
-      static_for<NSUB>([&](auto s_c) {
-        constexpr int s = decltype(s_c)::value;
-        static_for<FN * FM>([&](auto m_c) {
-          constexpr int m = decltype(m_c)::value, i = m / FM, j = m % FM;
-          acc[i][j] = mfma16<TIn>(xf[s][i], yf[s][j], (kFirst && s == 0) ? zero4 : acc[i][j]);
-        });
-      });
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_setprio(0);
-    };
-    // The lane index is re-read through an opaque move, so the epilogue's address arithmetic stays
-    // here instead of being hoisted into registers held across the K-loop.
-    auto epilogue = [&](auto edge_c) {
-      constexpr bool kEdge = decltype(edge_c)::value;
-      const int ln = (int)opaque_u32((unsigned)lane);
-      const int m_lane = m_base + (ln & 15), n_lane = col0 + TN * wn + 8 * (ln >> 4);
-      const unsigned voff = (unsigned)(m_lane * args.ldc + n_lane) * (unsigned)es;
-#pragma unroll
-      for (int pu = 0; pu < FN / 2; ++pu) {
-#pragma unroll
-        for (int j = 0; j < FM; ++j) {
-          float vv[8];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            vv[e] = acc[2 * pu][j][e];
-            vv[4 + e] = acc[2 * pu + 1][j][e];
-          }
-          if constexpr (kEdge)
-            store8<OUT, true>(vv, rc, m_lane + 16 * j, rows_left, n_lane + 32 * pu, N, args.ldc);
-          else
-            store8_at<OUT>(vv, rc, voff, (unsigned)((16 * j * args.ldc + 32 * pu) * es));
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-    };
-    const bool full_tile = rows_left >= BM && cols_left >= BN;
+    for (int j = 0; j < LB; ++j)
+      dma16_unseen(rb, sb + j * 1024, add_in_place(b0, (unsigned)(b_urow(j) * args.ldb) * 2u), 2u * k0);
+  };
+  // LDS byte offsets of the A and B tiles of K-tile g, from ring position p = 2g mod 5 (split) or
+  // g mod 2 (stages)
+  auto a_at = [&](int p) SPT_INLINE { return SPLIT ? p * A_BYTES : p * STAGE; };
+  auto b_at = [&](int p) SPT_INLINE { return SPLIT ? (p + 1 == S ? 0 : p + 1) * A_BYTES : p * STAGE + A_BYTES; };
+  auto pos_step = [&](int p, int n) SPT_INLINE {  // ring position of K-tile g+n
+    const int q = SPLIT ? p + 2 * n : p + n;
+    return q % S;
+  };
 
-    if (grp == 0) {
-      // ------------------------------------------------------------------------- G0
-      issue_a(a_at(0), 0);
-      issue_b(b_at(0), 0);
-      if (SPLIT && KT > 1) {
-        issue_a(a_at(1), 1);
-        wait_vmcnt<LA>();  // K-tile 0 landed; A(1) may be in flight
-      } else {
-        wait_vmcnt<0>();
-      }
-      barrier_sync();  // K-tile 0 visible
-      auto step = [&](int u, auto first_c) {
-        // phase 2u: memory
-        if (u + 1 < KT) {
-          if constexpr (SPLIT) issue_b(b_at(u + 1), u + 1);
-          else {
-            issue_a(a_at(u + 1), u + 1);
-            issue_b(b_at(u + 1), u + 1);
-          }
+  u32x4 xf[NSUB][FN], yf[NSUB][FM];  // the K-tile's fragments: B side (x), A side (y)
+  f32x4 acc[FN][FM];
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+
+  auto read_frags = [&](int p) SPT_INLINE {
+    const int pu = __builtin_amdgcn_readfirstlane(p);
+    const char* pa = smem + opaque_s32(a_at(pu));
+    const char* pb = smem + opaque_s32(b_at(pu));
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) {
+#pragma unroll
+      for (int f = 0; f < FN; ++f) xf[s][f] = *(const u32x4*)(pb + b_rd[s] + f * FRAG);
+#pragma unroll
+      for (int f = 0; f < FM; ++f) yf[s][f] = *(const u32x4*)(pa + a_rd[s] + f * FRAG);
+    }
+    wait_lgkmcnt0();
+  };
+  // the MFMAs of one K-tile; kFirst starts every chain from zero (accumulate = (k != 0))
+  auto compute = [&](auto first_c) SPT_INLINE {
+    constexpr bool kFirst = decltype(first_c)::value;
+    __builtin_amdgcn_s_setprio(1);
+    static_for<NSUB>([&](auto s_c) {
+      constexpr int s = decltype(s_c)::value;
+      static_for<FN * FM>([&](auto m_c) {
+        constexpr int m = decltype(m_c)::value, i = m / FM, j = m % FM;
+        acc[i][j] = mfma16<TIn>(xf[s][i], yf[s][j], (kFirst && s == 0) ? zero4 : acc[i][j]);
+      });
+    });
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
+  };
+  // Store this wave's part of output tile `tl` from the accumulators: fp32 -> output type, 8
+  // consecutive columns per lane. The lane index is re-read through an opaque move, so the address
+  // arithmetic stays here instead of being hoisted into registers held across the K-loop.
+  auto epilogue = [&](const PpTile& tl_in) SPT_INLINE {
+    PpTile tl;
+    tl.t = tl_in.t;
+    tl.row0 = __builtin_amdgcn_readfirstlane(tl_in.row0);
+    tl.col0 = __builtin_amdgcn_readfirstlane(tl_in.col0);
+    tl.rows_left = __builtin_amdgcn_readfirstlane(tl_in.rows_left);
+    tl.cols_left = __builtin_amdgcn_readfirstlane(tl_in.cols_left);
+    const __amdgpu_buffer_rsrc_t rc = c_rsrc(tl);
+    const int ln = (int)opaque_u32((unsigned)lane);
+    const int m_lane = m_base + (ln & 15), n_lane = tl.col0 + TN * wn + 8 * (ln >> 4);
+    const bool full = tl.rows_left >= BM && tl.cols_left >= BN;
+    const unsigned voff = (unsigned)(m_lane * args.ldc + n_lane) * (unsigned)es;
+#pragma unroll
+    for (int pu = 0; pu < FN / 2; ++pu) {
+#pragma unroll
+      for (int j = 0; j < FM; ++j) {
+        float vv[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          vv[e] = acc[2 * pu][j][e];
+          vv[4 + e] = acc[2 * pu + 1][j][e];
         }
-        read_frags(u);
-        barrier_sync();
-        // phase 2u+1: compute K-tile u, then make sure this group's loads for K-tile u+1 landed
-        compute(first_c);
-        wait_vmcnt<0>();
-        barrier_sync();
-      };
-      step(0, std::true_type{});
-      for (int u = 1; u < KT; ++u) step(u, std::false_type{});
-      // phase 2KT: epilogue, beside G1's last compute phase
-      if (full_tile) epilogue(std::false_type{});
-      else epilogue(std::true_type{});
-      barrier_sync();
+        if (full) store8_at<OUT>(vv, rc, voff, (unsigned)((16 * j * args.ldc + 32 * pu) * es));
+        else store8<OUT, true>(vv, rc, m_lane + 16 * j, tl.rows_left, n_lane + 32 * pu, N, args.ldc);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
+  using t_ = std::true_type;
+  using f_ = std::false_type;
+  PpTile prev;  // the output tile whose stores are pending
+  prev.t = args.num_tiles;
+
+  if (grp == 0) {
+    // --------------------------------------------------------------------------- G0
+    Cursor cur = cursor_at(u0);  // K-tile g
+    Cursor nx = cur;             // K-tile g+1
+    advance(nx);
+    issue_a(cur, a_at(0));
+    issue_b(cur, b_at(0));
+    if (SPLIT && valid(nx)) {
+      issue_a(nx, a_at(pos_step(0, 1)));
+      wait_vmcnt<LA>();  // K-tile 0 landed; A(1) may be in flight
     } else {
-      // ------------------------------------------------------------------------- G1
-      barrier_sync();  // K-tile 0 visible
-      barrier_sync();  // phase 0: idle
-      auto step = [&](int u, auto first_c) {
-        // phase 2u+1: memory
-        if (SPLIT && u + 2 < KT) issue_a(a_at(u + 2), u + 2);
-        read_frags(u);
+      wait_vmcnt<0>();
+    }
+    barrier_sync();  // K-tile 0 visible
+    int p = 0;       // ring position of K-tile g
+    auto step = [&](auto first_c) SPT_INLINE {
+      // phase 2g: memory. Load ahead, store the previous output tile, read K-tile g.
+      if (valid(nx)) {
+        const int q = pos_step(p, 1);
+        if constexpr (!SPLIT) issue_a(nx, a_at(q));
+        issue_b(nx, b_at(q));
+      }
+      if constexpr (decltype(first_c)::value) {
+        if (prev.t < args.num_tiles) epilogue(prev);
+      }
+      read_frags(p);
+      barrier_sync();
+      // phase 2g+1: compute K-tile g, then make sure this group's loads for K-tile g+1 (and the
+      // stores issued after them) are done
+      compute(first_c);
+      wait_vmcnt<0>();
+      barrier_sync();
+      p = pos_step(p, 1);
+      advance(nx);
+    };
+    for (; valid(cur); cur.tl = tile_at(cur.tl.t + args.grid)) {
+      step(t_{});
+      for (int u = 1; u < KT; ++u) step(f_{});
+      prev = cur.tl;
+    }
+    // phase 2G: the last tile's stores, beside G1's last compute phase
+    epilogue(prev);
+    barrier_sync();
+  } else {
+    // --------------------------------------------------------------------------- G1
+    Cursor cur = cursor_at(u0);  // K-tile g
+    Cursor n2 = cur;             // K-tile g+2
+    advance(n2);
+    advance(n2);
+    barrier_sync();  // K-tile 0 visible
+    barrier_sync();  // phase 0: idle
+    int p = 0;
+    auto step = [&](auto first_c) SPT_INLINE {
+      constexpr bool kFirst = decltype(first_c)::value;
+      // phase 2g+1: memory. Load A(g+2), read K-tile g, and make sure A(g+1) has landed, with
+      // A(g+2) possibly still in flight. In the first K-tile of an output tile the previous tile's
+      // stores go out here too; the wait then comes before them, so that the count of loads
+      // issued after A(g+1) stays exact.
+      bool loaded = false;
+      if constexpr (SPLIT) {
+        if (valid(n2)) {
+          issue_a(n2, a_at(pos_step(p, 2)));
+          loaded = true;
+        }
+      }
+      // A(g+1) landed: only the loads of A(g+2) may still be in flight
+      auto wait_a = [&]() SPT_INLINE {
         if constexpr (SPLIT) {
-          // A(u+1), loaded two phases ago, must have landed; A(u+2) may still be in flight
-          if (u + 2 < KT) wait_vmcnt<LA>();
+          if (loaded) wait_vmcnt<LA>();
           else wait_vmcnt<0>();
         }
-        barrier_sync();
-        // phase 2u+2: compute
-        compute(first_c);
-        barrier_sync();
       };
-      step(0, std::true_type{});
-      for (int u = 1; u < KT; ++u) step(u, std::false_type{});
-      // after the last barrier, beside G0's prologue of the next tile
-      if (full_tile) epilogue(std::false_type{});
-      else epilogue(std::true_type{});
+      if constexpr (kFirst) {
+        wait_a();
+        if (prev.t < args.num_tiles) epilogue(prev);
+      }
+      read_frags(p);
+      if constexpr (!kFirst) wait_a();
+      barrier_sync();
+      // phase 2g+2: compute
+      compute(first_c);
+      barrier_sync();
+      p = pos_step(p, 1);
+      advance(n2);
+    };
+    for (; valid(cur); cur.tl = tile_at(cur.tl.t + args.grid)) {
+      step(t_{});
+      for (int u = 1; u < KT; ++u) step(f_{});
+      prev = cur.tl;
     }
+    epilogue(prev);  // after the last barrier
   }
 }
 
