@@ -179,6 +179,19 @@ gemm_status_t gemm_probe_copy(const void* src, void* dst, int64_t bytes, void* s
  */
 gemm_status_t gemm_probe_lds_read(int swizzle, int64_t iters, void* stream);
 
+/*
+ * Launch a global->LDS fill kernel (the staging path of the GEMM's mainloop): one workgroup of
+ * 4 waves per CU; per iteration every wave issues 16 direct 1 KiB loads (buffer_load_dwordx4 ...
+ * lds), two iterations in flight. Workgroup w reads the `region` bytes of src at w*region,
+ * wrapping inside them; when region times the CU count exceeds `bytes`, every workgroup reads the
+ * first `region` bytes instead. A small region keeps the reads L2-resident, a large one streams.
+ * *bytes_moved receives the bytes the launch loads into LDS.
+ * Errors: GEMM_ERR_INVALID (null pointer, iters < 1, bytes outside [64 KiB, 2^31 - 64 KiB], region
+ * not a multiple of 64 KiB or larger than bytes), GEMM_ERR_HIP.
+ */
+gemm_status_t gemm_probe_fill(const void* src, int64_t bytes, int64_t region, int64_t iters, void* stream,
+                              double* bytes_moved);
+
 #ifdef __cplusplus
 }
 #endif

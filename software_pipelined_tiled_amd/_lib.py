@@ -19,7 +19,7 @@ GEMM_LOAD_AUTO, GEMM_LOAD_DMA, GEMM_LOAD_REG = 0, 1, 2
 # every entry point include/gemm.h declares
 EXPORTS = ("gemm_plan_create", "gemm_run", "gemm_plan_destroy", "gemm_plan_describe", "gemm_status_string",
            "gemm_select_config", "gemm_schedule_tile", "gemm_lds_chunk_offset", "gemm_probe_mfma_peak",
-           "gemm_probe_copy", "gemm_probe_lds_read")
+           "gemm_probe_copy", "gemm_probe_lds_read", "gemm_probe_fill")
 
 
 class GemmLibraryMissing(ImportError):
@@ -82,6 +82,8 @@ def lib() -> ctypes.CDLL:
     L.gemm_probe_copy.argtypes = [vp, vp, i64, vp]
     L.gemm_probe_lds_read.restype = i32
     L.gemm_probe_lds_read.argtypes = [i32, i64, vp]
+    L.gemm_probe_fill.restype = i32
+    L.gemm_probe_fill.argtypes = [vp, i64, i64, i64, vp, P(ctypes.c_double)]
     _lib = L
     return L
 
@@ -161,3 +163,10 @@ def gemm_probe_copy(src_ptr: int, dst_ptr: int, nbytes: int, stream: int = 0) ->
 
 def gemm_probe_lds_read(swizzle: int, iters: int, stream: int = 0) -> None:
     _check(lib().gemm_probe_lds_read(swizzle, iters, stream or None), "gemm_probe_lds_read")
+
+
+def gemm_probe_fill(src_ptr: int, nbytes: int, region: int, iters: int, stream: int = 0) -> float:
+    moved = ctypes.c_double()
+    _check(lib().gemm_probe_fill(src_ptr, nbytes, region, iters, stream or None, ctypes.byref(moved)),
+           "gemm_probe_fill")
+    return moved.value

@@ -64,6 +64,30 @@ __global__ void __launch_bounds__(256) lds_read_kernel(unsigned* sink, int sw, i
   if ((acc[0] ^ acc[1] ^ acc[2] ^ acc[3]) == 0x12345678u) sink[0] = 1u;  // keeps the reads alive
 }
 
+// Global->LDS fill probe: one workgroup of 4 waves per CU; each wave issues 16 direct 1 KiB
+// loads (buffer_load_dwordx4 ... lds) per iteration into its own 16 KiB of LDS, keeping two
+// iterations in flight. Workgroup w reads the `region` bytes at w*region (or all read the first
+// `region` bytes when `shared`), wrapping inside them.
+typedef __attribute__((address_space(3))) void lds_void_t;
+__global__ void __launch_bounds__(256) fill_kernel(const char* src, unsigned nbytes, unsigned region, int shared,
+                                                   int64_t iters) {
+  __shared__ __attribute__((aligned(1024))) char lds[64 * 1024];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(src), (short)0, (int)nbytes, 0x00020000);
+  const unsigned base = shared ? 0u : blockIdx.x * region;
+  for (int64_t it = 0; it < iters; ++it) {
+    const unsigned it_off = (unsigned)(((uint64_t)it * 65536u) % region);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const unsigned off = base + ((it_off + (unsigned)(w * 16 + j) * 1024u) % region) + 16u * lane;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(lds + (w * 16 + j) * 1024), 16, off, 0, 0, 0);
+    }
+    if (it & 1) __builtin_amdgcn_s_waitcnt(0);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+}
+
 float* g_sink[64] = {};
 
 }  // namespace
@@ -106,5 +130,21 @@ extern "C" gemm_status_t gemm_probe_lds_read(int swizzle, int64_t iters, void* s
   hipLaunchKernelGGL(lds_read_kernel, dim3(cu), dim3(256), 0, (hipStream_t)stream, (unsigned*)g_sink[dev], swizzle,
                      iters);
   if (hipGetLastError() != hipSuccess) return GEMM_ERR_HIP;
+  return GEMM_OK;
+}
+
+extern "C" gemm_status_t gemm_probe_fill(const void* src, int64_t bytes, int64_t region, int64_t iters, void* stream,
+                                         double* bytes_moved) {
+  if (!src || !bytes_moved || iters < 1 || bytes < 65536 || bytes > 0x7FFF0000LL || region < 65536 ||
+      region % 65536 != 0 || region > bytes)
+    return GEMM_ERR_INVALID;
+  int dev = 0, cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return GEMM_ERR_HIP;
+  if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return GEMM_ERR_HIP;
+  const int shared = region * cu > bytes ? 1 : 0;  // otherwise every workgroup has a region of its own
+  hipLaunchKernelGGL(fill_kernel, dim3(cu), dim3(256), 0, (hipStream_t)stream, (const char*)src, (unsigned)bytes,
+                     (unsigned)region, shared, iters);
+  if (hipGetLastError() != hipSuccess) return GEMM_ERR_HIP;
+  *bytes_moved = (double)cu * (double)iters * 65536.0;
   return GEMM_OK;
 }

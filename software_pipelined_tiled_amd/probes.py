@@ -3,6 +3,8 @@
     peak    dense MFMA throughput (16x16x32 bf16) in TFLOP/s, 1 and 2 waves per SIMD
     copy    16-byte streaming copy bandwidth in GB/s (read + write)
     lds     the LDS read-pattern kernels, one launch per swizzle (read the counters with rocprofv3)
+    fill    global->LDS fill rate per CU: each workgroup re-reading its own 64 KiB (L2-resident),
+            and streaming 4 MiB of its own (L2 misses)
 """
 from __future__ import annotations
 
@@ -39,6 +41,19 @@ def copy(nbytes: int = 1 << 30) -> float:
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
+def fill(iters: int = 2000) -> dict:
+    nbytes = 1 << 30
+    src = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    res = {}
+    for name, region in (("l2_resident_64KiB_per_cu", 1 << 16), ("streaming_4MiB_per_cu", 1 << 22)):
+        _lib.gemm_probe_fill(src.data_ptr(), nbytes, region, 8)
+        ms, moved = _timed(lambda: _lib.gemm_probe_fill(src.data_ptr(), nbytes, region, iters))
+        res[name + "_GBps_total"] = moved / (ms * 1e-3) / 1e9
+        res[name + "_B_per_ns_per_cu"] = moved / (ms * 1e6) / cus
+    return res
+
+
 def lds(iters: int = 2000) -> None:
     for sw in (-1, 0, 1, 2, 3, 4):
         _lib.gemm_probe_lds_read(sw, iters)
@@ -51,6 +66,8 @@ if __name__ == "__main__":
         print(peak())
     elif what == "copy":
         print(f"{copy():.1f} GB/s")
+    elif what == "fill":
+        print(fill())
     elif what == "lds":
         lds()
         print("lds probes launched: swizzles -1, 0, 1, 2, 3, 4 in this order")

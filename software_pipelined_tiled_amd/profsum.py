@@ -9,6 +9,11 @@
         `bench.py --copy-calibration`. Each counter is scaled by what it reads for the 1 GiB copy
         kernel launched in the same run (which moves exactly 2^30 bytes each way).
 
+    python -m software_pipelined_tiled_amd.profsum clock COUNTER_CSV AGENT_CSV BENCH_JSON OUT_MD --command CMD
+        average shader clock of each GEMM launch (SQ_BUSY_CYCLES, summed over the shader engines,
+        over the launch's duration) and the MFMA utilisation at that clock; the flop count comes
+        from SQ_INSTS_VALU_MFMA_MOPS_BF16 or _F16 (512 flop each) and is checked against 2MNK
+
     python -m software_pipelined_tiled_amd.profsum lds COUNTER_CSV OUT_MD --command CMD
         bank-conflict ratio SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE of each LDS read-pattern probe
         launched by `python3 -m software_pipelined_tiled_amd.probes lds` (swizzles -1, 0 .. 4 in order)
@@ -147,6 +152,47 @@ def traffic(fetch_csv: str, write_csv: str, bench_json: str, out_json: str, comm
     print(json.dumps(d, indent=1))
 
 
+def clock(counter_csv: str, agent_csv: str, bench_json: str, out_md: str, command: str) -> None:
+    line = _bench_line(bench_json)
+    c = line["config"]
+    pre = kernel_prefix(c["plan"])
+    gpu = next(r for r in _rows(agent_csv) if r.get("Agent_Type") == "GPU")
+    n_se, n_cu = int(gpu["Num_Shader_Banks"]), int(gpu["Cu_Count"])
+    fmax = float(gpu["Max_Engine_Clk_Fcompute"]) * 1e6
+    per = {}
+    for r in _rows(counter_csv):
+        if pre not in r["Kernel_Name"]:
+            continue
+        d = per.setdefault(int(r["Dispatch_Id"]), {"dur": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9})
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+    flop_exact = 2.0 * c["M"] * c["N"] * c["K"]
+    out = [f"# Shader clock and MFMA utilisation: {c['workload']} ({c['M']}x{c['N']}x{c['K']}, "
+           f"{c['in_dtype']} -> {c['out_dtype']})", "",
+           f"Command: `{command}`", "",
+           f"Kernel: `{c['kernel']}`; {n_cu} CUs, {n_se} shader engines, peak engine clock {fmax / 1e9:.2f} GHz.",
+           "clock = SQ_BUSY_CYCLES / shader engines / duration; MFMA utilisation = achieved flop rate / "
+           "(CUs x 4096 flop/clk x clock).", "",
+           "| dispatch | duration (us) | TFLOP/s | clock (GHz) | MFMA util. at that clock | at peak clock | MFMA flop / 2MNK |",
+           "|---|---|---|---|---|---|---|"]
+    rows = []
+    for i, (did, d) in enumerate(sorted(per.items())):
+        mops = d.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) + d.get("SQ_INSTS_VALU_MFMA_MOPS_F16", 0.0)
+        tf = flop_exact / d["dur"] / 1e12
+        clk = d["SQ_BUSY_CYCLES"] / n_se / d["dur"]
+        util = flop_exact / d["dur"] / (n_cu * 4096 * clk)
+        rows.append((tf, clk, util))
+        out.append(f"| {did}{' (first)' if i == 0 else ''} | {d['dur'] * 1e6:.1f} | {tf:.1f} | {clk / 1e9:.3f} | "
+                   f"{util:.3f} | {tf * 1e12 / (n_cu * 4096 * fmax):.3f} | {mops * 512 / flop_exact:.3f} |")
+    if len(rows) > 1:
+        rest = rows[1:]
+        out += ["", f"Mean over the launches after the first: {statistics.mean(r[0] for r in rest):.1f} TFLOP/s at "
+                    f"{statistics.mean(r[1] for r in rest) / 1e9:.3f} GHz, MFMA utilisation "
+                    f"{statistics.mean(r[2] for r in rest):.3f} at that clock."]
+    with open(out_md, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print("\n".join(out))
+
+
 LDS_PATTERNS = {-1: "linear 16*lane (reference)", 0: "none (f = 0)", 1: "row % 8 (the pages' 128-byte swizzle)",
                 2: "(row % 8) XOR bit3(row)", 3: "(row / 2) % 8", 4: "(row % 4) XOR (bit2(row) << 2)"}
 
@@ -183,12 +229,17 @@ def main(argv=None) -> int:
     t = sub.add_parser("traffic")
     t.add_argument("fetch_csv"), t.add_argument("write_csv"), t.add_argument("bench_json"), t.add_argument("out_json")
     t.add_argument("--command", required=True)
+    ck = sub.add_parser("clock")
+    ck.add_argument("counter_csv"), ck.add_argument("agent_csv"), ck.add_argument("bench_json"), ck.add_argument("out_md")
+    ck.add_argument("--command", required=True)
     d = sub.add_parser("lds")
     d.add_argument("counter_csv"), d.add_argument("out_md")
     d.add_argument("--command", required=True)
     a = ap.parse_args(argv)
     if a.what == "lds":
         lds(a.counter_csv, a.out_md, a.command)
+    elif a.what == "clock":
+        clock(a.counter_csv, a.agent_csv, a.bench_json, a.out_md, a.command)
     elif a.what == "kernel-stats":
         kernel_stats(a.stats_csv, a.bench_json, a.out_md, a.command)
     else:
