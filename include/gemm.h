@@ -17,11 +17,18 @@
  *
  * Ownership and threading.
  *   - A plan is created by gemm_plan_create, owned by the caller, immutable after creation, and
- *     freed by gemm_plan_destroy. It holds no device memory.
+ *     freed by gemm_plan_destroy.
+ *   - A plan owns a device workspace, allocated on the current device by gemm_plan_create and
+ *     freed by gemm_plan_destroy, when its configuration splits K (fp32 partial planes: splits x
+ *     M x roundup(N, 8) x 4 bytes) or stages its operands (load_path GEMM_LOAD_STAGED: copies of
+ *     A and B with rows of roundup(K, 8) elements); otherwise it holds no device memory.
+ *     gemm_plan_workspace_bytes reports the size.
  *   - A, B and C are caller-owned device pointers; they must stay valid until the work enqueued
  *     by gemm_run has completed on its stream.
  *   - gemm_run only enqueues kernels on `stream` (a hipStream_t; NULL is the default stream). It
- *     neither allocates nor synchronises, so one plan may be run concurrently on several streams.
+ *     neither allocates nor synchronises. A plan without a workspace may be run concurrently on
+ *     several streams; runs of a plan with a workspace share it and must not overlap (run them on
+ *     one stream, or order them with events, or make one plan per stream).
  *
  * Errors. Every entry point returns a gemm_status_t; nothing aborts or throws across the ABI.
  * A failed kernel launch returns GEMM_ERR_HIP. Misalignment is never an error: it only selects
@@ -43,14 +50,17 @@ typedef enum {
   GEMM_ERR_INVALID = -1,     /* a null out-pointer, negative size, ld too small, bad config */
   GEMM_ERR_UNSUPPORTED = -2, /* dtype combination or size this library does not handle */
   GEMM_ERR_HIP = -3,         /* a HIP runtime call or kernel launch failed */
-  GEMM_ERR_NOMEM = -4        /* host allocation of the plan failed */
+  GEMM_ERR_NOMEM = -4        /* allocating the plan or its device workspace failed */
 } gemm_status_t;
 
 /* How the K-loop stages operand tiles into LDS. */
 typedef enum {
   GEMM_LOAD_AUTO = 0, /* DMA when pointers, lda/ldb and K allow it, else REG */
   GEMM_LOAD_DMA = 1,  /* direct global->LDS buffer loads (16-byte chunks, needs alignment) */
-  GEMM_LOAD_REG = 2   /* global->VGPR->LDS copies with per-element K masking (any alignment) */
+  GEMM_LOAD_REG = 2,  /* global->VGPR->LDS copies with per-element K masking (any alignment) */
+  GEMM_LOAD_STAGED = 3 /* copy A and B into workspace rows of roundup(K, 8) elements (zero
+                          padded), then DMA; any alignment. AUTO takes it when DMA is not
+                          possible and the copies fit in 3 GiB */
 } gemm_load_path_t;
 
 /*
@@ -69,6 +79,11 @@ typedef enum {
  *   load_path    gemm_load_path_t
  *   grid         workgroups launched (describe only; 0 in an override means "from the device")
  *   lds_bytes    LDS per workgroup (describe only)
+ *   splits       split-K: K ranges per output tile, 1..16 (0 in an override means 1). Each range
+ *                of ceil(ceil(K/bk)/splits) K-tiles is a work unit of its own writing an fp32
+ *                partial plane; a second kernel adds the planes in range order and rounds once.
+ *                The built-in choice splits when the output tiles alone leave workgroup slots of
+ *                the device idle. DMA and staged paths only
  */
 typedef struct {
   int bm, bn, bk;
@@ -80,6 +95,7 @@ typedef struct {
   int load_path;
   int grid;
   int lds_bytes;
+  int splits;
 } gemm_config_t;
 
 typedef struct gemm_plan_s* gemm_plan_t;
@@ -93,8 +109,9 @@ typedef struct gemm_plan_s* gemm_plan_t;
  *   lda >= K, ldb >= K, ldc >= N   leading dimensions in elements
  *   config    NULL for the built-in choice, else an explicit configuration (validated)
  * Errors: GEMM_ERR_INVALID (null out, bad sizes or ld, invalid override),
- *         GEMM_ERR_UNSUPPORTED (dtype pair, a tile whose row span exceeds 2^31 bytes),
- *         GEMM_ERR_HIP (no usable gfx950 device), GEMM_ERR_NOMEM.
+ *         GEMM_ERR_UNSUPPORTED (dtype pair, a tile whose row span exceeds 2^31 bytes, an override
+ *         whose workspace exceeds the caps: 1 GiB of partial planes, 3 GiB of staged operands),
+ *         GEMM_ERR_HIP (no usable gfx950 device), GEMM_ERR_NOMEM (host or device allocation).
  */
 gemm_status_t gemm_plan_create(gemm_plan_t* out, int64_t M, int64_t N, int64_t K,
                                gemm_dtype_t a_dtype, gemm_dtype_t b_dtype, gemm_dtype_t c_dtype,
@@ -104,13 +121,20 @@ gemm_status_t gemm_plan_create(gemm_plan_t* out, int64_t M, int64_t N, int64_t K
  * Enqueue C = A·Bᵀ on `stream` (hipStream_t, NULL = default stream).
  *   A: M rows of lda elements, B: N rows of ldb elements, C: M rows of ldc elements; only
  *   C[i*ldc + j] with i < M, j < N is written (the ldc padding is never touched).
- *   If A or B is not 16-byte aligned the register-staged path runs instead of the DMA path.
+ *   If A or B is not 16-byte aligned the register-staged path runs instead of the DMA path
+ *   (a staged plan copies the operands and needs no alignment).
+ *   A staged plan launches the staging copy first; a split plan launches the mainloop into its
+ *   partial planes and then the reduction, all on `stream`.
  * Errors: GEMM_ERR_INVALID (null plan; null A, B or C while M, N > 0), GEMM_ERR_HIP (launch).
  */
 gemm_status_t gemm_run(gemm_plan_t plan, const void* A, const void* B, void* C, void* stream);
 
-/* Free a plan. NULL is accepted and returns GEMM_OK. */
+/* Free a plan and its workspace. NULL is accepted and returns GEMM_OK. Work enqueued with the
+ * plan must have completed. GEMM_ERR_HIP if freeing the workspace failed (the plan is freed). */
 gemm_status_t gemm_plan_destroy(gemm_plan_t plan);
+
+/* Bytes of device workspace the plan owns (0 when none). Errors: GEMM_ERR_INVALID on NULL. */
+gemm_status_t gemm_plan_workspace_bytes(gemm_plan_t plan, int64_t* out);
 
 /* Copy the configuration `plan` launches into *out. Errors: GEMM_ERR_INVALID on NULL. */
 gemm_status_t gemm_plan_describe(gemm_plan_t plan, gemm_config_t* out);
@@ -134,13 +158,15 @@ gemm_status_t gemm_select_config(int64_t M, int64_t N, int64_t K, gemm_dtype_t a
                                  gemm_config_t* out);
 
 /*
- * Output tile handled by workgroup `wg` (0 <= wg < grid) on its `round`-th pass of the
- * persistent loop, for a tiles_m x tiles_n tile grid, grouped raster of height group_m, and
- * `grid` workgroups (dispatched round-robin over the 8 XCDs). Writes (*tm, *tn) and returns 1,
- * or returns 0 when that workgroup has no tile in that round. Invalid arguments return -1.
+ * Work unit handled by workgroup `wg` (0 <= wg < grid) on its `round`-th pass of the persistent
+ * loop, for a tiles_m x tiles_n tile grid with `splits` K ranges per tile, grouped raster of
+ * height group_m, and `grid` workgroups (dispatched round-robin over the 8 XCDs): output tile
+ * (*tm, *tn), K range *split. Units are numbered range by range (all tiles of range 0 in raster
+ * order, then range 1, ...). Returns 1, or 0 when that workgroup has no unit in that round.
+ * Invalid arguments return -1.
  */
-int gemm_schedule_tile(int64_t tiles_m, int64_t tiles_n, int group_m, int grid, int wg, int round,
-                       int64_t* tm, int64_t* tn);
+int gemm_schedule_tile(int64_t tiles_m, int64_t tiles_n, int splits, int group_m, int grid, int wg,
+                       int round, int64_t* tm, int64_t* tn, int* split);
 
 /*
  * Byte offset, inside one LDS operand tile of `rows` rows and depth bk (32, 64 or 128), of the

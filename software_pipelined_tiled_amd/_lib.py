@@ -14,10 +14,11 @@ LIB_PATH = os.path.join(HERE, "libsptgemm.so")
 
 GEMM_F16, GEMM_BF16, GEMM_F32 = 0, 1, 2
 GEMM_OK, GEMM_ERR_INVALID, GEMM_ERR_UNSUPPORTED, GEMM_ERR_HIP, GEMM_ERR_NOMEM = 0, -1, -2, -3, -4
-GEMM_LOAD_AUTO, GEMM_LOAD_DMA, GEMM_LOAD_REG = 0, 1, 2
+GEMM_LOAD_AUTO, GEMM_LOAD_DMA, GEMM_LOAD_REG, GEMM_LOAD_STAGED = 0, 1, 2, 3
 
 # every entry point include/gemm.h declares
-EXPORTS = ("gemm_plan_create", "gemm_run", "gemm_plan_destroy", "gemm_plan_describe", "gemm_status_string",
+EXPORTS = ("gemm_plan_create", "gemm_run", "gemm_plan_destroy", "gemm_plan_describe", "gemm_plan_workspace_bytes",
+           "gemm_status_string",
            "gemm_select_config", "gemm_schedule_tile", "gemm_lds_chunk_offset", "gemm_probe_mfma_peak",
            "gemm_probe_copy", "gemm_probe_lds_read", "gemm_probe_fill")
 
@@ -34,7 +35,7 @@ class GemmError(RuntimeError):
 
 class GemmConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in ("bm", "bn", "bk", "stages", "waves", "mfma", "persistent", "group_m",
-                                            "load_path", "grid", "lds_bytes")]
+                                            "load_path", "grid", "lds_bytes", "splits")]
 
     def as_dict(self) -> dict:
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -68,12 +69,14 @@ def lib() -> ctypes.CDLL:
     L.gemm_plan_destroy.argtypes = [vp]
     L.gemm_plan_describe.restype = i32
     L.gemm_plan_describe.argtypes = [vp, P(GemmConfig)]
+    L.gemm_plan_workspace_bytes.restype = i32
+    L.gemm_plan_workspace_bytes.argtypes = [vp, P(i64)]
     L.gemm_status_string.restype = ctypes.c_char_p
     L.gemm_status_string.argtypes = [i32]
     L.gemm_select_config.restype = i32
     L.gemm_select_config.argtypes = [i64, i64, i64, i32, i32, i32, i64, i64, i64, i32, i32, P(GemmConfig)]
     L.gemm_schedule_tile.restype = i32
-    L.gemm_schedule_tile.argtypes = [i64, i64, i32, i32, i32, i32, P(i64), P(i64)]
+    L.gemm_schedule_tile.argtypes = [i64, i64, i32, i32, i32, i32, i32, P(i64), P(i64), P(i32)]
     L.gemm_lds_chunk_offset.restype = i64
     L.gemm_lds_chunk_offset.argtypes = [i32, i32, i32, i32]
     L.gemm_probe_mfma_peak.restype = i32
@@ -123,6 +126,12 @@ def gemm_plan_describe(plan: int) -> dict:
     return c.as_dict()
 
 
+def gemm_plan_workspace_bytes(plan: int) -> int:
+    n = ctypes.c_int64()
+    _check(lib().gemm_plan_workspace_bytes(plan, ctypes.byref(n)), "gemm_plan_workspace_bytes")
+    return n.value
+
+
 def gemm_select_config(M, N, K, a_dtype, b_dtype, c_dtype, lda, ldb, ldc, cu_count=256, lds_bytes=160 * 1024) -> dict:
     c = GemmConfig()
     _check(lib().gemm_select_config(M, N, K, a_dtype, b_dtype, c_dtype, lda, ldb, ldc, cu_count, lds_bytes,
@@ -137,13 +146,14 @@ def gemm_select_config_status(M, N, K, a_dtype, b_dtype, c_dtype, lda, ldb, ldc,
                                     ctypes.byref(c))
 
 
-def gemm_schedule_tile(tiles_m, tiles_n, group_m, grid, wg, rnd):
-    """(tm, tn) for workgroup `wg` in round `rnd`, None if it has no tile; raises on invalid args."""
-    tm, tn = ctypes.c_int64(), ctypes.c_int64()
-    r = lib().gemm_schedule_tile(tiles_m, tiles_n, group_m, grid, wg, rnd, ctypes.byref(tm), ctypes.byref(tn))
+def gemm_schedule_tile(tiles_m, tiles_n, splits, group_m, grid, wg, rnd):
+    """(tm, tn, split) for workgroup `wg` in round `rnd`, None if it has no unit; raises on invalid args."""
+    tm, tn, sp = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int()
+    r = lib().gemm_schedule_tile(tiles_m, tiles_n, splits, group_m, grid, wg, rnd, ctypes.byref(tm),
+                                 ctypes.byref(tn), ctypes.byref(sp))
     if r < 0:
         raise GemmError(GEMM_ERR_INVALID, "gemm_schedule_tile")
-    return (tm.value, tn.value) if r == 1 else None
+    return (tm.value, tn.value, sp.value) if r == 1 else None
 
 
 def gemm_lds_chunk_offset(rows: int, bk: int, row: int, chunk: int) -> int:

@@ -23,7 +23,7 @@ COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
           "-I" + INCLUDE, "-I" + CSRC]
 # per-source extra flags
 EXTRA = {"spt_probe.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
-SOURCES = ["spt_gemm.hip", "spt_gemm_pp.hip", "spt_gemm_reg.hip", "spt_probe.hip", "spt_api.cpp"]
+SOURCES = ["spt_gemm.hip", "spt_gemm_pp.hip", "spt_gemm_reg.hip", "spt_splitk_stage.hip", "spt_probe.hip", "spt_api.cpp"]
 
 
 def _compile(src: str, verbose: bool) -> str:

@@ -15,20 +15,56 @@ struct gemm_plan_s {
   int64_t M, N, K, lda, ldb, ldc;
   gemm_dtype_t in_dtype, out_dtype;
   gemm_config_t cfg;       // what gemm_run launches on the preferred path
-  const void* fn_main;     // kernel for cfg (DMA or REG)
+  const void* fn_main;     // mainloop kernel for cfg (DMA or REG; fp32 output when K is split)
   gemm_config_t cfg_reg;   // register-staged fallback used when pointers are misaligned
   const void* fn_reg;
   int tiles_m, tiles_n;
   int tiles_m_reg, tiles_n_reg;
+  // workspace (device memory owned by the plan): staged operands, then the split-K partial planes
+  int dev;
+  char* ws;
+  int64_t kp;              // K as the mainloop sees it: K, or K rounded up to 8 when staged
+  int64_t stage_a_off, stage_b_off, part_off;  // byte offsets inside ws
+  int64_t ldw;             // row length of a partial plane (elements)
+  const void* fn_reduce;
+  const void* fn_stage;
 };
 
 namespace {
 
 constexpr int kMaxLds = 160 * 1024;
+constexpr int kMaxSplits = 16;
+constexpr int kMinKtPerSplit = 8;                           // K-tiles a split-K unit keeps at least
+constexpr int64_t kMaxPartialBytes = (int64_t)1 << 30;      // fp32 partial planes of a split-K plan
+constexpr int64_t kMaxStageBytes = (int64_t)3 << 30;        // staged copies of A and B
 
 bool valid_in(gemm_dtype_t d) { return d == GEMM_F16 || d == GEMM_BF16; }
 bool valid_out(gemm_dtype_t d) { return d == GEMM_F16 || d == GEMM_BF16 || d == GEMM_F32; }
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+bool is_dma(int path) { return path == GEMM_LOAD_DMA || path == GEMM_LOAD_STAGED; }
+
+// Workspace layout: staged A (M rows of kp elements), staged B (N rows), then `splits` fp32 planes
+// of M rows of ldw = N rounded up to 8 elements; each part starts on a 256-byte boundary.
+struct WsLayout {
+  int64_t stage_a, stage_b, part, total, kp, ldw;
+};
+WsLayout ws_layout(int64_t M, int64_t N, int64_t K, int path, int splits) {
+  WsLayout w{};
+  const bool staged = path == GEMM_LOAD_STAGED;
+  w.kp = staged ? round_up(K, 8) : K;
+  w.ldw = round_up(N, 8);
+  const int64_t a_bytes = staged ? round_up(M * w.kp * 2, 256) : 0;
+  const int64_t b_bytes = staged ? round_up(N * w.kp * 2, 256) : 0;
+  w.stage_a = 0;
+  w.stage_b = a_bytes;
+  w.part = a_bytes + b_bytes;
+  w.total = w.part + (splits > 1 ? (int64_t)splits * M * w.ldw * 4 : 0);
+  return w;
+}
+int64_t stage_bytes(int64_t M, int64_t N, int64_t K) { return ws_layout(M, N, K, GEMM_LOAD_STAGED, 1).total; }
+int64_t partial_bytes(int64_t M, int64_t N, int splits) { return splits > 1 ? (int64_t)splits * M * round_up(N, 8) * 4 : 0; }
+
 
 gemm_status_t check_args(int64_t M, int64_t N, int64_t K, gemm_dtype_t a, gemm_dtype_t b, gemm_dtype_t c,
                          int64_t lda, int64_t ldb, int64_t ldc) {
@@ -57,7 +93,7 @@ const spt::KernelEntry* find_entry(const spt::KernelEntry* t, int n, const gemm_
 
 const spt::KernelEntry* find_entry_for_path(const gemm_config_t& c) {
   int n = 0;
-  if (c.load_path == GEMM_LOAD_REG) {
+  if (!is_dma(c.load_path)) {
     const spt::KernelEntry* t = spt::reg_kernel_table(&n);
     return find_entry(t, n, c);
   }
@@ -85,24 +121,66 @@ int groups_per_cu(const gemm_config_t& c, int lds_bytes) {
   return g < 1 ? 1 : g;
 }
 
-// Preferred tiles, largest first; the first that yields at least one tile per CU wins. The 256x256
-// tile runs on the two-wave-group kernel (8 waves) with the split ring of five operand slots.
-struct Candidate { int bm, bn, bk, stages, waves; };
-const Candidate kDmaMenu[] = {{256, 256, 64, 5, 8}, {256, 128, 64, 3, 4}, {128, 128, 64, 4, 4}, {64, 64, 64, 4, 4}};
-const Candidate kRegMenu[] = {{128, 128, 64, 2, 4}, {64, 64, 64, 2, 4}};
+// K ranges per output tile (split-K): enough work units (tiles x splits) to give every workgroup
+// slot of the device one, while each range keeps at least kMinKtPerSplit K-tiles, no range is empty
+// and the fp32 partial planes stay under kMaxPartialBytes. 1 when the tiles alone fill the device.
+int pick_splits(const gemm_config_t& c, int64_t M, int64_t N, int64_t K, int cu_count, int lds_bytes) {
+  if (!is_dma(c.load_path) || K == 0) return 1;
+  const int64_t tiles = ceil_div(M, c.bm) * ceil_div(N, c.bn);
+  const int64_t slots = (int64_t)cu_count * groups_per_cu(c, lds_bytes);
+  if (tiles >= slots) return 1;
+  const int64_t kt = ceil_div(K, c.bk);
+  int64_t s = slots / tiles;
+  if (s > kt / kMinKtPerSplit) s = kt / kMinKtPerSplit;
+  if (s > kMaxSplits) s = kMaxSplits;
+  while (s > 1 && ((s - 1) * ceil_div(kt, s) >= kt || partial_bytes(M, N, (int)s) > kMaxPartialBytes)) --s;
+  return s < 1 ? 1 : (int)s;
+}
 
-gemm_config_t choose(int64_t M, int64_t N, const Candidate* menu, int n, int path, int cu_count, int lds_bytes) {
+// The tile menu, with each kernel's sustained MFMA rate per CU relative to the two-wave-group
+// 256x256 kernel (measured on large square problems: about 1450, 1160, 1020 and 500 TFLOP/s).
+struct Candidate { int bm, bn, bk, stages, waves; double rate; };
+const Candidate kDmaMenu[] = {{256, 256, 64, 5, 8, 1.0}, {256, 128, 64, 3, 4, 0.8}, {128, 128, 64, 4, 4, 0.7},
+                              {64, 64, 64, 4, 4, 0.35}};
+const Candidate kRegMenu[] = {{128, 128, 64, 2, 4, 0.35}, {64, 64, 64, 2, 4, 0.2}};
+
+// Modelled time of a configuration (seconds): the rounds of work units every workgroup slot runs,
+// each unit its MFMA work at the kernel's rate plus about one K-tile of fill and store, and, for a
+// split K, the fp32 partial planes written and read back by the reduction.
+constexpr double kCuFlops = 1450e12 / 256;  // two-wave-group kernel, per CU
+constexpr double kHbmBytes = 4.5e12;        // streaming rate of the reduction
+double model_time(const gemm_config_t& c, double rate, int64_t M, int64_t N, int64_t K, int cu_count,
+                  int lds_bytes) {
+  const int gpc = groups_per_cu(c, lds_bytes);
+  const int64_t units = ceil_div(M, c.bm) * ceil_div(N, c.bn) * c.splits;
+  const int64_t rounds = ceil_div(units, (int64_t)cu_count * gpc);
+  const int64_t kt_per = ceil_div(ceil_div(K, c.bk), c.splits);
+  const double unit = 2.0 * c.bm * c.bn * (double)(kt_per + 1) * c.bk / (rate * kCuFlops / gpc);
+  const double reduce = c.splits > 1 ? (2.0 * partial_bytes(M, N, c.splits) + 2.0 * M * N) / kHbmBytes : 0.0;
+  return rounds * unit + reduce;
+}
+
+// The candidate of least modelled time, each with K unsplit and with K split as pick_splits says. A
+// tile whose padded grid is more than half padding is passed over (unless it is the last).
+gemm_config_t choose(int64_t M, int64_t N, int64_t K, const Candidate* menu, int n, int path, int cu_count,
+                     int lds_bytes) {
   gemm_config_t best{};
-  int64_t best_tiles = -1;
+  double best_t = 0.0;
+  bool have = false;
   for (int i = 0; i < n; ++i) {
     const Candidate& c = menu[i];
-    const int64_t tiles = ceil_div(M, c.bm) * ceil_div(N, c.bn);
+    const int64_t tm = ceil_div(M, c.bm), tn = ceil_div(N, c.bn);
+    if (i + 1 < n && 2 * M * N < tm * c.bm * tn * c.bn) continue;
     gemm_config_t cfg{};
     cfg.bm = c.bm; cfg.bn = c.bn; cfg.bk = c.bk; cfg.stages = c.stages; cfg.waves = c.waves; cfg.mfma = 16;
     cfg.persistent = 1; cfg.group_m = 8; cfg.load_path = path;
     cfg.lds_bytes = ring_bytes(cfg);
-    if (tiles >= cu_count) return cfg;
-    if (tiles > best_tiles) { best = cfg; best_tiles = tiles; }
+    const int split = pick_splits(cfg, M, N, K, cu_count, lds_bytes);
+    for (int sp : {1, split}) {
+      cfg.splits = sp;
+      const double t = model_time(cfg, c.rate, M, N, K, cu_count, lds_bytes);
+      if (!have || t < best_t) { best = cfg; best_t = t; have = true; }
+    }
   }
   return best;
 }
@@ -110,22 +188,24 @@ gemm_config_t choose(int64_t M, int64_t N, const Candidate* menu, int n, int pat
 void finish_config(gemm_config_t& c, int64_t M, int64_t N, int cu_count, int lds_bytes, int& tm, int& tn) {
   tm = (int)ceil_div(M, c.bm);
   tn = (int)ceil_div(N, c.bn);
-  const int64_t tiles = (int64_t)tm * tn;
+  if (c.splits < 1) c.splits = 1;
+  const int64_t units = (int64_t)tm * tn * c.splits;
   c.lds_bytes = ring_bytes(c);
   if (c.group_m < 1) c.group_m = 8;
   if (c.persistent) {
     int64_t g = c.grid > 0 ? c.grid : (int64_t)cu_count * groups_per_cu(c, lds_bytes);
-    if (g > tiles) g = tiles;
+    if (g > units) g = units;
     c.grid = (int)(g < 1 ? 1 : g);
   } else {
-    c.grid = (int)(tiles < 1 ? 1 : tiles);
+    c.grid = (int)(units < 1 ? 1 : units);
   }
 }
 
 gemm_status_t validate_override(const gemm_config_t& c) {
   if (c.mfma != 16 && c.mfma != 0) return GEMM_ERR_INVALID;
-  if (c.load_path < GEMM_LOAD_AUTO || c.load_path > GEMM_LOAD_REG) return GEMM_ERR_INVALID;
+  if (c.load_path < GEMM_LOAD_AUTO || c.load_path > GEMM_LOAD_STAGED) return GEMM_ERR_INVALID;
   if (c.group_m < 0 || c.grid < 0) return GEMM_ERR_INVALID;
+  if (c.splits < 0 || c.splits > kMaxSplits) return GEMM_ERR_INVALID;
   return GEMM_OK;
 }
 
@@ -136,28 +216,42 @@ gemm_status_t select_impl(int64_t M, int64_t N, int64_t K, gemm_dtype_t a, gemm_
   if (st != GEMM_OK) return st;
   if (cu_count < 1 || lds_bytes < 1) return GEMM_ERR_INVALID;
   const bool dma_ok = dma_eligible(K, lda, ldb);
+  const bool stage_ok = stage_bytes(M, N, K) <= kMaxStageBytes;
   gemm_config_t cfg;
   if (ovr) {
     st = validate_override(*ovr);
     if (st != GEMM_OK) return st;
     cfg = *ovr;
     if (cfg.mfma == 0) cfg.mfma = 16;
-    if (cfg.load_path == GEMM_LOAD_AUTO) cfg.load_path = dma_ok ? GEMM_LOAD_DMA : GEMM_LOAD_REG;
+    if (cfg.splits == 0) cfg.splits = 1;
+    if (cfg.load_path == GEMM_LOAD_AUTO)
+      cfg.load_path = dma_ok ? GEMM_LOAD_DMA : (stage_ok ? GEMM_LOAD_STAGED : GEMM_LOAD_REG);
     if (cfg.load_path == GEMM_LOAD_DMA && !dma_ok) return GEMM_ERR_INVALID;
+    if (cfg.load_path == GEMM_LOAD_STAGED && !stage_ok) return GEMM_ERR_UNSUPPORTED;
+    if (cfg.load_path == GEMM_LOAD_REG && cfg.splits > 1) return GEMM_ERR_INVALID;
+    if (partial_bytes(M, N, cfg.splits) > kMaxPartialBytes) return GEMM_ERR_UNSUPPORTED;
     cfg.lds_bytes = ring_bytes(cfg);
     if (!find_entry_for_path(cfg)) return GEMM_ERR_INVALID;
     if (cfg.lds_bytes > lds_bytes) return GEMM_ERR_INVALID;
   } else if (dma_ok) {
-    cfg = choose(M, N, kDmaMenu, 4, GEMM_LOAD_DMA, cu_count, lds_bytes);
+    cfg = choose(M, N, K, kDmaMenu, 4, GEMM_LOAD_DMA, cu_count, lds_bytes);
+  } else if (stage_ok) {
+    cfg = choose(M, N, round_up(K, 8), kDmaMenu, 4, GEMM_LOAD_STAGED, cu_count, lds_bytes);
   } else {
-    cfg = choose(M, N, kRegMenu, 2, GEMM_LOAD_REG, cu_count, lds_bytes);
+    cfg = choose(M, N, K, kRegMenu, 2, GEMM_LOAD_REG, cu_count, lds_bytes);
   }
   int tm, tn;
   finish_config(cfg, M, N, cu_count, lds_bytes, tm, tn);
-  if (!offsets_fit(cfg, lda, ldb, ldc, c)) return GEMM_ERR_UNSUPPORTED;
+  // the mainloop reads staged operands with rows of kp elements, and a split run writes fp32
+  // planes with rows of ldw elements
+  const WsLayout w = ws_layout(M, N, K, cfg.load_path, cfg.splits);
+  const bool staged = cfg.load_path == GEMM_LOAD_STAGED;
+  if (!offsets_fit(cfg, staged ? w.kp : lda, staged ? w.kp : ldb, ldc, c)) return GEMM_ERR_UNSUPPORTED;
+  if (cfg.splits > 1 && !offsets_fit(cfg, staged ? w.kp : lda, staged ? w.kp : ldb, w.ldw, GEMM_F32))
+    return GEMM_ERR_UNSUPPORTED;
   *out = cfg;
   if (out_reg) {
-    gemm_config_t r = choose(M, N, kRegMenu, 2, GEMM_LOAD_REG, cu_count, lds_bytes);
+    gemm_config_t r = choose(M, N, K, kRegMenu, 2, GEMM_LOAD_REG, cu_count, lds_bytes);
     r.persistent = cfg.persistent;
     r.group_m = cfg.group_m;
     finish_config(r, M, N, cu_count, lds_bytes, tm, tn);
@@ -214,28 +308,80 @@ gemm_status_t gemm_plan_create(gemm_plan_t* out, int64_t M, int64_t N, int64_t K
   if (!p) return GEMM_ERR_NOMEM;
   p->M = M; p->N = N; p->K = K; p->lda = lda; p->ldb = ldb; p->ldc = ldc;
   p->in_dtype = a_dtype; p->out_dtype = c_dtype;
+  p->dev = dev;
   st = select_impl(M, N, K, a_dtype, b_dtype, c_dtype, lda, ldb, ldc, cu, lds, config, &p->cfg, &p->cfg_reg);
   if (st != GEMM_OK) { delete p; return st; }
-  p->fn_main = kernel_fn(p->cfg, a_dtype, c_dtype);
+  const bool split = p->cfg.splits > 1;
+  p->fn_main = kernel_fn(p->cfg, a_dtype, split ? GEMM_F32 : c_dtype);
   p->fn_reg = kernel_fn(p->cfg_reg, a_dtype, c_dtype);
+  p->fn_reduce = split ? spt::splitk_reduce_fn((int)c_dtype) : nullptr;
+  p->fn_stage = p->cfg.load_path == GEMM_LOAD_STAGED ? spt::stage_fn() : nullptr;
   p->tiles_m = (int)ceil_div(M, p->cfg.bm);
   p->tiles_n = (int)ceil_div(N, p->cfg.bn);
   p->tiles_m_reg = (int)ceil_div(M, p->cfg_reg.bm);
   p->tiles_n_reg = (int)ceil_div(N, p->cfg_reg.bn);
   if (!p->fn_main) { delete p; return GEMM_ERR_UNSUPPORTED; }
+  const WsLayout w = ws_layout(M, N, K, p->cfg.load_path, p->cfg.splits);
+  p->kp = w.kp;
+  p->ldw = w.ldw;
+  p->stage_a_off = w.stage_a;
+  p->stage_b_off = w.stage_b;
+  p->part_off = w.part;
+  if (w.total > 0 && M > 0 && N > 0) {
+    void* ws = nullptr;
+    if (hipMalloc(&ws, (size_t)w.total) != hipSuccess) {
+      (void)hipGetLastError();
+      delete p;
+      return GEMM_ERR_NOMEM;
+    }
+    p->ws = (char*)ws;
+  }
   *out = p;
   return GEMM_OK;
 }
 
 gemm_status_t gemm_plan_destroy(gemm_plan_t plan) {
+  if (!plan) return GEMM_OK;
+  gemm_status_t st = GEMM_OK;
+  if (plan->ws) {
+    int cur = 0;
+    const bool switched = hipGetDevice(&cur) == hipSuccess && cur != plan->dev && hipSetDevice(plan->dev) == hipSuccess;
+    if (hipFree(plan->ws) != hipSuccess) {
+      (void)hipGetLastError();
+      st = GEMM_ERR_HIP;
+    }
+    if (switched) (void)hipSetDevice(cur);
+  }
   delete plan;
-  return GEMM_OK;
+  return st;
 }
 
 gemm_status_t gemm_plan_describe(gemm_plan_t plan, gemm_config_t* out) {
   if (!plan || !out) return GEMM_ERR_INVALID;
   *out = plan->cfg;
   return GEMM_OK;
+}
+
+gemm_status_t gemm_plan_workspace_bytes(gemm_plan_t plan, int64_t* out) {
+  if (!plan || !out) return GEMM_ERR_INVALID;
+  *out = plan->ws ? ws_layout(plan->M, plan->N, plan->K, plan->cfg.load_path, plan->cfg.splits).total : 0;
+  return GEMM_OK;
+}
+
+static gemm_status_t launch(const void* fn, int grid, int threads, void* arg, void* stream) {
+  void* kargs[] = {arg};
+  if (hipLaunchKernel(fn, dim3(grid), dim3(threads), kargs, 0, (hipStream_t)stream) != hipSuccess) {
+    (void)hipGetLastError();
+    return GEMM_ERR_HIP;
+  }
+  return GEMM_OK;
+}
+
+// blocks of 256 threads for a streaming pass over `chunks` 8-element chunks: one chunk per thread,
+// at most 16 blocks per CU's worth (the kernels loop over the rest)
+static int stream_grid(int64_t chunks) {
+  const int64_t b = ceil_div(chunks, 256);
+  return (int)(b < 1 ? 1 : (b > 4096 ? 4096 : b));
 }
 
 gemm_status_t gemm_run(gemm_plan_t plan, const void* A, const void* B, void* C, void* stream) {
@@ -246,41 +392,72 @@ gemm_status_t gemm_run(gemm_plan_t plan, const void* A, const void* B, void* C, 
   const gemm_config_t* cfg = &plan->cfg;
   const void* fn = plan->fn_main;
   int tm = plan->tiles_m, tn = plan->tiles_n;
-  if (plan->cfg.load_path == GEMM_LOAD_DMA && !aligned) {
+  int64_t K = plan->K, lda = plan->lda, ldb = plan->ldb;
+  gemm_status_t st;
+  if (cfg->load_path == GEMM_LOAD_STAGED) {
+    if (K > 0) {
+      spt::StageArgs g;
+      g.A = A; g.B = B;
+      g.dA = plan->ws + plan->stage_a_off;
+      g.dB = plan->ws + plan->stage_b_off;
+      g.rows_a = (int)plan->M; g.rows_b = (int)plan->N; g.K = (int)K;
+      g.lda = (int)lda; g.ldb = (int)ldb; g.ldd = (int)plan->kp;
+      st = launch(plan->fn_stage, stream_grid((plan->M + plan->N) * (plan->kp / 8)), 256, &g, stream);
+      if (st != GEMM_OK) return st;
+      A = g.dA;
+      B = g.dB;
+      K = lda = ldb = plan->kp;
+    }
+  } else if (cfg->load_path == GEMM_LOAD_DMA && !aligned) {
     if (!plan->fn_reg) return GEMM_ERR_UNSUPPORTED;
     cfg = &plan->cfg_reg;
     fn = plan->fn_reg;
     tm = plan->tiles_m_reg;
     tn = plan->tiles_n_reg;
   }
+  const int splits = cfg->splits > 1 ? cfg->splits : 1;
   spt::GemmArgs args;
   args.A = A; args.B = B; args.C = C;
-  args.M = (int)plan->M; args.N = (int)plan->N; args.K = (int)plan->K;
-  args.lda = (int)plan->lda; args.ldb = (int)plan->ldb; args.ldc = (int)plan->ldc;
-  args.tiles_m = tm; args.tiles_n = tn; args.num_tiles = tm * tn;
+  args.M = (int)plan->M; args.N = (int)plan->N; args.K = (int)K;
+  args.lda = (int)lda; args.ldb = (int)ldb; args.ldc = (int)plan->ldc;
+  args.tiles_m = tm; args.tiles_n = tn; args.num_tiles = tm * tn * splits;
   args.group_m = cfg->group_m;
   args.grid = cfg->grid;
   args.out_dtype = (int)plan->out_dtype;
-  void* kargs[] = {&args};
-  hipError_t e = hipLaunchKernel(fn, dim3(cfg->grid), dim3(64 * cfg->waves), kargs, 0, (hipStream_t)stream);
-  if (e != hipSuccess) {
-    (void)hipGetLastError();
-    return GEMM_ERR_HIP;
+  args.splits = splits;
+  args.kt_per = (int)ceil_div(ceil_div(K, cfg->bk), splits);
+  args.split_stride = 0;
+  if (splits > 1) {
+    args.C = plan->ws + plan->part_off;
+    args.ldc = (int)plan->ldw;
+    args.out_dtype = (int)GEMM_F32;
+    args.split_stride = (long long)plan->M * plan->ldw * 4;
   }
-  return GEMM_OK;
+  st = launch(fn, cfg->grid, 64 * cfg->waves, &args, stream);
+  if (st != GEMM_OK || splits == 1) return st;
+  spt::ReduceArgs r;
+  r.W = (const float*)(plan->ws + plan->part_off);
+  r.plane = (long long)plan->M * plan->ldw;
+  r.splits = splits;
+  r.M = (int)plan->M; r.N = (int)plan->N; r.ldw = (int)plan->ldw;
+  r.C = C;
+  r.ldc = (int)plan->ldc;
+  return launch(plan->fn_reduce, stream_grid(plan->M * ceil_div(plan->N, 8)), 256, &r, stream);
 }
 
-int gemm_schedule_tile(int64_t tiles_m, int64_t tiles_n, int group_m, int grid, int wg, int round, int64_t* tm,
-                       int64_t* tn) {
-  if (tiles_m < 1 || tiles_n < 1 || group_m < 1 || grid < 1 || wg < 0 || wg >= grid || round < 0 || !tm || !tn)
+int gemm_schedule_tile(int64_t tiles_m, int64_t tiles_n, int splits, int group_m, int grid, int wg, int round,
+                       int64_t* tm, int64_t* tn, int* split) {
+  if (tiles_m < 1 || tiles_n < 1 || splits < 1 || group_m < 1 || grid < 1 || wg < 0 || wg >= grid || round < 0 ||
+      !tm || !tn || !split)
     return -1;
-  if (tiles_m * tiles_n > INT32_MAX) return -1;
+  if (tiles_m * tiles_n * splits > INT32_MAX) return -1;
   const int64_t t = (int64_t)round * grid + spt::xcd_remap(wg, grid);
-  if (t >= tiles_m * tiles_n) return 0;
-  int m, n;
-  spt::grouped_raster((int)t, (int)tiles_m, (int)tiles_n, group_m, m, n);
+  if (t >= tiles_m * tiles_n * splits) return 0;
+  int m, n, s;
+  spt::unit_decode((int)t, (int)tiles_m, (int)tiles_n, group_m, m, n, s);
   *tm = m;
   *tn = n;
+  *split = s;
   return 1;
 }
 

@@ -74,17 +74,30 @@ SPT_HD int b_row_perm(int rho) {
   return base + 8 * g + 4 * h + i;
 }
 
+// Split-K work units. With `splits` K ranges per output tile, a launch has tiles_m * tiles_n *
+// splits work units; unit t computes K range s = t / (tiles_m * tiles_n) of output tile number
+// t mod (tiles_m * tiles_n) in the grouped raster, so units of one K range run side by side and
+// share operand bands in L2 just as whole tiles do. Range s covers K-tiles [s*kt_per, (s+1)*kt_per).
+SPT_HD void unit_decode(int t, int tiles_m, int tiles_n, int group_m, int& tm, int& tn, int& s) {
+  const int per = tiles_m * tiles_n;
+  s = t / per;
+  grouped_raster(t - s * per, tiles_m, tiles_n, group_m, tm, tn);
+}
+
 // Kernel arguments (passed by value).
 struct GemmArgs {
   const void* A;
   const void* B;
-  void* C;
+  void* C;  // output, or the fp32 partial planes of a split-K run
   int M, N, K;
   int lda, ldb, ldc;
-  int tiles_m, tiles_n, num_tiles;
+  int tiles_m, tiles_n, num_tiles;  // num_tiles: work units, tiles_m * tiles_n * splits
   int group_m;
   int grid;
   int out_dtype;  // 0 f16, 1 bf16, 2 f32
+  int splits;     // K ranges per output tile (1: the whole K in one unit)
+  int kt_per;     // K-tiles per work unit
+  long long split_stride;  // bytes from the partial plane of K range s to that of s + 1
 };
 
 }  // namespace spt

@@ -37,7 +37,7 @@ __global__ void __launch_bounds__(WM* WN * 64, 1) gemm_dma_kernel(GemmArgs args)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / WN, wn = wave % WN;
   const int M = args.M, N = args.N, K = args.K;
-  const int KT = (K + BK - 1) / BK;
+  const int KT = args.kt_per;  // K-tiles per work unit (all of K unless K is split)
 
   // DMA address map. A instruction j of this wave fills LDS bytes [(wave*LA + j) * 1024, +1024)
   // of the stage's A region: rows rho = RPI*rb + lane/CPR of row group g (RPI = 8 rows of 128
@@ -83,9 +83,10 @@ __global__ void __launch_bounds__(WM* WN * 64, 1) gemm_dma_kernel(GemmArgs args)
   const int u = xcd_remap(blockIdx.x, args.grid);
   bool first_tile = true;
   for (int t = u; t < args.num_tiles; t += args.grid) {
-    int tm, tn;
-    grouped_raster(t, args.tiles_m, args.tiles_n, args.group_m, tm, tn);
+    int tm, tn, ks;
+    unit_decode(t, args.tiles_m, args.tiles_n, args.group_m, tm, tn, ks);
     const int row0 = tm * BM, col0 = tn * BN;
+    const int kbase = ks * KT * BK;  // first K element of this unit's range
     const int rows_left = M - row0, cols_left = N - col0;
     const bool full_tile = rows_left >= BM && cols_left >= BN;
     const __amdgpu_buffer_rsrc_t ra =
@@ -109,15 +110,15 @@ __global__ void __launch_bounds__(WM* WN * 64, 1) gemm_dma_kernel(GemmArgs args)
       b_off[j] = row < cols_left ? (unsigned)(row * args.ldb + T::GK * g + lane_kc) * 2u : kOOB;
     }
 
-    // DMA instruction d (0 .. LW-1: A loads first, then B) of this wave's share of K-tile kt,
-    // into ring slot `slot`. The K offset rides in the scalar soffset; the per-lane voffset is a
+    // DMA instruction d (0 .. LW-1: A loads first, then B) of this wave's share of K-tile kt of
+    // the unit's range (absolute K offset k0 = kbase + kt*BK). The K offset rides in the scalar soffset; the per-lane voffset is a
     // constant, replaced by one past num_records (reads zero) when the lane's chunk lies at or past
     // K (lane_kc >= K - k0 - GK*g: one compare per group and K-tile). K-tiles past the end are
     // therefore zero-filling dummies, and every hand-over issues exactly LW loads per wave, which
     // keeps every vmcnt threshold constant. (kOOB + soffset stays past num_records: soffset < 2^31.)
     // `dst` gives the LDS byte offsets of the A and B tiles' destinations.
     auto dma_one = [&](Regions dst, int kt, int d) {
-      const int k0 = kt * BK;
+      const int k0 = kt * BK + kbase;
       if (d < T::LA) {
         const int g = (wave * T::LA + d) / (BM / T::RPI);
         char* sa = smem + dst.a + (wave * T::LA + d) * 1024;
@@ -246,8 +247,8 @@ __global__ void __launch_bounds__(WM* WN * 64, 1) gemm_dma_kernel(GemmArgs args)
     };
 
     const int es = OUT == 2 ? 4 : 2;
-    const __amdgpu_buffer_rsrc_t rc =
-        make_rsrc((char*)args.C + (size_t)row0 * args.ldc * es, ((uint64_t)(rows_left - 1) * args.ldc + N) * es);
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc((char*)args.C + (size_t)ks * args.split_stride + (size_t)row0 * args.ldc * es,
+                                                ((uint64_t)(rows_left - 1) * args.ldc + N) * es);
 
     if (KT == 0) {  // empty sum: C = 0
       const float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};

@@ -20,11 +20,12 @@
 // inside a group the four waves form a 2x2 grid of 64x128 wave tiles (128 fp32 accumulators per
 // lane).
 //
-// The phases run on without a break from one output tile to the next: number the K-tiles a
-// workgroup computes g = 0, 1, ..., G-1 across all its output tiles (KT per tile). K-tile g is read
-// in phases 2g (G0) and 2g+1 (G1) and computed in phases 2g+1 (G0) and 2g+2 (G1). Loads run ahead
-// into the next output tile the same way they run ahead inside one, so there is no prologue per
-// output tile (the pages' "overlap load k+1 with compute k and store k-1" carried across tiles).
+// The phases run on without a break from one work unit (an output tile, or one K range of it when
+// K is split) to the next: number the K-tiles a workgroup computes g = 0, 1, ..., G-1 across all
+// its units (KT per unit). K-tile g is read in phases 2g (G0) and 2g+1 (G1) and computed in phases
+// 2g+1 (G0) and 2g+2 (G1). Loads run ahead into the next unit the same way they run ahead inside
+// one, so there is no prologue per unit: the pages' overlap of the next tile's loads with the
+// current math and the previous tile's stores, carried across tiles.
 // A group stores a finished output tile in its next memory phase, before reading the next
 // fragments; after the last K-tile G0 stores in phase 2G, beside G1's last MFMAs, and G1 after
 // the last barrier. Both groups pass 2G + 2 barriers.
@@ -42,10 +43,12 @@
 
 namespace spt {
 
-// One output tile of the raster (t >= num_tiles: past the end of this workgroup's list).
+// One work unit: an output tile of the raster and the K range it covers (t >= num_tiles: past the
+// end of this workgroup's list).
 struct PpTile {
   int t;
   int row0, col0, rows_left, cols_left;
+  int ks, kb;  // K range index and its first K element
 };
 
 template <int S, typename TIn, int OUT>
@@ -69,15 +72,17 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmArgs args) {
   const int grp = wave >> 2, v = wave & 3;
   const int wm = v >> 1, wn = v & 1;
   const int M = args.M, N = args.N, K = args.K;
-  const int KT = (K + BK - 1) / BK;
+  const int KT = args.kt_per;  // K-tiles per work unit
   const int es = OUT == 2 ? 4 : 2;
   const int m_base = 128 * grp + TM * wm;  // this wave's first output row inside a tile
 
   auto tile_at = [&](int t) SPT_INLINE {
     PpTile tl;
     tl.t = t;
-    int tm = 0, tn = 0;
-    if (t < args.num_tiles) grouped_raster(t, args.tiles_m, args.tiles_n, args.group_m, tm, tn);
+    int tm = 0, tn = 0, ks = 0;
+    if (t < args.num_tiles) unit_decode(t, args.tiles_m, args.tiles_n, args.group_m, tm, tn, ks);
+    tl.ks = ks;
+    tl.kb = ks * KT * BK;
     tl.row0 = tm * BM;
     tl.col0 = tn * BN;
     tl.rows_left = M - tl.row0;
@@ -85,7 +90,7 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmArgs args) {
     return tl;
   };
   auto c_rsrc = [&](const PpTile& tl) SPT_INLINE {
-    return make_rsrc((char*)args.C + (size_t)tl.row0 * args.ldc * es,
+    return make_rsrc((char*)args.C + (size_t)tl.ks * args.split_stride + (size_t)tl.row0 * args.ldc * es,
                      ((uint64_t)(tl.rows_left - 1) * args.ldc + N) * es);
   };
 
@@ -147,7 +152,7 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmArgs args) {
   // lies at or beyond the descriptor's num_records and reads zero. A chunk at or past K is moved
   // beyond num_records explicitly (one select per call); the K offset rides in the scalar offset.
   auto issue_a = [&](const Cursor& c, int dst) SPT_INLINE {
-    const int k0 = __builtin_amdgcn_readfirstlane(c.u) * BK;
+    const int k0 = __builtin_amdgcn_readfirstlane(c.u) * BK + __builtin_amdgcn_readfirstlane(c.tl.kb);
     const int row0 = __builtin_amdgcn_readfirstlane(c.tl.row0);
     const int rows_left = __builtin_amdgcn_readfirstlane(c.tl.rows_left);
     const __amdgpu_buffer_rsrc_t ra = make_rsrc((const char*)args.A + (size_t)row0 * args.lda * 2,
@@ -159,7 +164,7 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmArgs args) {
       dma16_unseen(ra, sa + j * 1024, add_in_place(a0, (unsigned)(a_urow(j) * args.lda) * 2u), 2u * k0);
   };
   auto issue_b = [&](const Cursor& c, int dst) SPT_INLINE {
-    const int k0 = __builtin_amdgcn_readfirstlane(c.u) * BK;
+    const int k0 = __builtin_amdgcn_readfirstlane(c.u) * BK + __builtin_amdgcn_readfirstlane(c.tl.kb);
     const int col0 = __builtin_amdgcn_readfirstlane(c.tl.col0);
     const int cols_left = __builtin_amdgcn_readfirstlane(c.tl.cols_left);
     const __amdgpu_buffer_rsrc_t rb = make_rsrc((const char*)args.B + (size_t)col0 * args.ldb * 2,
@@ -220,6 +225,8 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmArgs args) {
     tl.col0 = __builtin_amdgcn_readfirstlane(tl_in.col0);
     tl.rows_left = __builtin_amdgcn_readfirstlane(tl_in.rows_left);
     tl.cols_left = __builtin_amdgcn_readfirstlane(tl_in.cols_left);
+    tl.ks = __builtin_amdgcn_readfirstlane(tl_in.ks);
+    tl.kb = 0;
     const __amdgpu_buffer_rsrc_t rc = c_rsrc(tl);
     const int ln = (int)opaque_u32((unsigned)lane);
     const int m_lane = m_base + (ln & 15), n_lane = tl.col0 + TN * wn + 8 * (ln >> 4);

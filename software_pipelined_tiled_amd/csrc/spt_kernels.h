@@ -13,4 +13,28 @@ const KernelEntry* dma_kernel_table(int* count);
 const KernelEntry* reg_kernel_table(int* count);
 const KernelEntry* pp_kernel_table(int* count);  // two wave groups (waves = 8), DMA loads
 
+// Split-K reduction: C (M x N, ldc, output type) from `splits` fp32 partial planes at W, W + plane,
+// ... (elements), each M rows of ldw elements (ldw a multiple of 8, W 16-byte aligned).
+struct ReduceArgs {
+  const float* W;
+  long long plane;
+  int splits;
+  int M, N, ldw;
+  void* C;
+  int ldc;
+};
+const void* splitk_reduce_fn(int out_dtype);  // __global__ void(ReduceArgs), 256 threads
+
+// Operand staging: rows_a rows of A (lda) and rows_b rows of B (ldb), K elements each, into dA and
+// dB with rows of ldd elements (ldd a multiple of 8 and >= K, dA and dB 16-byte aligned), the
+// columns from K to ldd zero.
+struct StageArgs {
+  const void* A;
+  const void* B;
+  void* dA;
+  void* dB;
+  int rows_a, rows_b, K, lda, ldb, ldd;
+};
+const void* stage_fn();  // __global__ void(StageArgs), 256 threads
+
 }  // namespace spt

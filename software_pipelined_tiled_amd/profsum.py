@@ -56,17 +56,22 @@ def kernel_source_hash() -> str:
 
 def kernel_prefix(plan: dict) -> str:
     """Start of the demangled template name of the kernel a plan launches."""
-    if plan["load_path"] == 1 and plan["waves"] == 8:
+    if plan["load_path"] != 2 and plan["waves"] == 8:
         return f"gemm_pp_kernel<{plan['stages']}, "
-    kind = "dma" if plan["load_path"] == 1 else "reg"
+    kind = "reg" if plan["load_path"] == 2 else "dma"
     return f"gemm_{kind}_kernel<{plan['bm']}, {plan['bn']}, {plan['bk']}, "
 
 
 def kernel_label(plan: dict, in_dt: str, out_dt: str) -> str:
-    """Short name of the kernel a plan launches, with its configuration."""
-    kind = "reg" if plan["load_path"] != 1 else ("pp" if plan["waves"] == 8 else "dma")
+    """Short name of the mainloop kernel a plan launches, with its configuration (a split-K plan's
+    mainloop writes fp32 partial planes)."""
+    kind = "reg" if plan["load_path"] == 2 else ("pp" if plan["waves"] == 8 else "dma")
+    splits = plan.get("splits", 1)
+    out = "f32" if splits > 1 else out_dt
+    extra = f",splits={splits}" if splits > 1 else ""
+    extra += ",staged" if plan["load_path"] == 3 else ""
     return (f"gemm_{kind}_kernel<{plan['bm']},{plan['bn']},{plan['bk']},{plan['stages']},"
-            f"waves={plan['waves']},{in_dt},{out_dt}>")
+            f"waves={plan['waves']},{in_dt},{out}{extra}>")
 
 
 def _bench_line(path: str) -> dict:

@@ -34,6 +34,9 @@ class Plan:
     def describe(self) -> dict:
         return _lib.gemm_plan_describe(self.handle)
 
+    def workspace_bytes(self) -> int:
+        return _lib.gemm_plan_workspace_bytes(self.handle)
+
     def run_ptrs(self, a_ptr: int, b_ptr: int, c_ptr: int, stream: int | None = None) -> None:
         if stream is None:
             stream = torch.cuda.current_stream().cuda_stream
@@ -73,10 +76,12 @@ def matmul(A: torch.Tensor, B: torch.Tensor, out_dtype: torch.dtype | None = Non
     N = B.shape[0]
     out_dtype = out_dtype or A.dtype
     C = out if out is not None else torch.empty((M, N), dtype=out_dtype, device=A.device)
+    # a plan with a workspace must not run on two streams at once: one cached plan per stream
+    stream = torch.cuda.current_stream(A.device).cuda_stream
     key = (M, N, K, A.dtype, out_dtype, A.stride(0), B.stride(0), C.stride(0),
-           tuple(sorted(config.items())) if config else None, A.device.index)
+           tuple(sorted(config.items())) if config else None, A.device.index, stream)
     plan = _plan_cache.get(key)
     if plan is None:
         plan = Plan(M, N, K, A.dtype, out_dtype, A.stride(0), B.stride(0), C.stride(0), config)
         _plan_cache[key] = plan
-    return plan.run(A, B, C)
+    return plan.run(A, B, C, stream)

@@ -36,9 +36,9 @@ REG_CONFIGS = [(128, 128, 2), (64, 64, 2)]
 RING_CONFIGS = [(64, 5, 4), (32, 4, 4), (64, 5, 8), (64, 2, 8)]
 
 
-def cfg(bm, bn, s, path=spt.GEMM_LOAD_DMA, persistent=1, group_m=8, grid=0, bk=64, waves=4):
+def cfg(bm, bn, s, path=spt.GEMM_LOAD_DMA, persistent=1, group_m=8, grid=0, bk=64, waves=4, splits=1):
     return dict(bm=bm, bn=bn, bk=bk, stages=s, waves=waves, mfma=16, persistent=persistent, group_m=group_m,
-                load_path=path, grid=grid, lds_bytes=0)
+                load_path=path, grid=grid, lds_bytes=0, splits=splits)
 
 
 def ring_cfg(bk, s, waves, **kw):
@@ -111,7 +111,7 @@ def test_output_dtypes_bit_exact(in_dt, out_dt):
     a = ints(M, K, in_dt, 7)
     b = ints(N, K, in_dt, 8)
     for c_cfg in (cfg(256, 256, 2), cfg(128, 128, 4), cfg(128, 128, 2, path=spt.GEMM_LOAD_REG),
-                  ring_cfg(64, 5, 8), ring_cfg(64, 5, 4)):
+                  ring_cfg(64, 5, 8), ring_cfg(64, 5, 4), ring_cfg(64, 5, 8, splits=3), cfg(64, 64, 4, splits=2)):
         c, _ = run_gpu(a, b, K, in_dt, out_dt, config=c_cfg)
         check_full(a, b, K, in_dt, out_dt, c, N, exact=True)
 
@@ -178,6 +178,96 @@ def test_deterministic_and_grouping_invariant():
     c3, _ = run_gpu(a, b, K, si.BF16, si.BF16, config=cfg(128, 128, 4, group_m=1, persistent=0))
     assert np.array_equal(c1, c2) and np.array_equal(c1, c3)  # tile order does not change any sum
     check_full(a, b, K, si.BF16, si.BF16, c1, N)
+
+
+# ------------------------------------------------------------------------- split-K and staging
+
+# (bm, bn, bk, stages, waves) of every mainloop kernel that runs split-K units
+SPLIT_CONFIGS = [(64, 64, 64, 4, 4), (128, 128, 64, 4, 4), (256, 128, 64, 3, 4), (256, 256, 64, 2, 4),
+                 (256, 256, 64, 5, 4), (256, 256, 32, 4, 4), (256, 256, 64, 5, 8), (256, 256, 64, 2, 8)]
+
+
+@pytest.mark.parametrize("bm,bn,bk,s,waves", SPLIT_CONFIGS)
+@pytest.mark.parametrize("splits", [2, 3, 5])
+def test_split_k_bit_exact(bm, bn, bk, s, waves, splits):
+    # ragged 2 x 2 tiles; 13 K-tiles of 64 (26 of 32) plus a tail, cut into ranges of unequal use
+    M, N, K = bm + bm // 2 + 5, 2 * bn - 9, 13 * 64 + 40
+    for in_dt in (si.F16, si.BF16):
+        a = ints(M, K, in_dt, 900 + bm + s + splits)
+        b = ints(N, K, in_dt, 950 + bn + waves + splits)
+        for grid in (0, 3):
+            c, desc = run_gpu(a, b, K, in_dt, si.F32,
+                              config=cfg(bm, bn, s, bk=bk, waves=waves, splits=splits, grid=grid))
+            assert desc["splits"] == splits
+            check_full(a, b, K, in_dt, si.F32, c, N, exact=True)
+
+
+@pytest.mark.parametrize("K,splits", [(64, 2), (320, 4), (320, 6), (8, 3), (136, 16), (1000, 7)])
+def test_split_k_uneven_and_empty_ranges(K, splits):
+    # K-tiles not a multiple of the ranges; with more ranges than K-tiles the last ones are empty
+    # and must contribute zeros
+    M, N = 100, 140
+    for conf in (cfg(64, 64, 4, splits=splits), ring_cfg(64, 5, 8, splits=splits)):
+        a = ints(M, K, si.BF16, K + splits)
+        b = ints(N, K, si.BF16, K + 2 * splits)
+        for out_dt in (si.BF16, si.F32):
+            c, _ = run_gpu(a, b, K, si.BF16, out_dt, config=conf)
+            check_full(a, b, K, si.BF16, out_dt, c, N, exact=True)
+
+
+def test_split_k_padded_ldc_and_no_out_of_bounds_writes():
+    M, N, K = 130, 75, 2048
+    a = ints(M, K, si.F16, 61)
+    b = ints(N, K, si.F16, 62)
+    for out_dt in (si.F16, si.F32):
+        ldc = N + 13  # odd row length: the reduction's unaligned-row stores
+        c, desc = run_gpu(a, b, K, si.F16, out_dt, ldc=ldc, config=cfg(64, 64, 4, splits=4))
+        assert desc["splits"] == 4
+        check_full(a, b, K, si.F16, out_dt, c, N, exact=True)
+        pad = orc.decode(out_dt, c[:, N:]) if out_dt != si.F32 else c[:, N:]
+        assert np.all(np.isnan(pad)), "the ldc padding of C was written"
+
+
+def test_split_k_real_values_deterministic():
+    M, N, K = 96, 1000, 8192
+    a = si.make_matrix(M, K, si.F16, "uniform", 71)
+    b = si.make_matrix(N, K, si.F16, "uniform", 72)
+    conf = cfg(64, 64, 4, splits=8)
+    c1, _ = run_gpu(a, b, K, si.F16, si.F16, config=conf)
+    c2, _ = run_gpu(a, b, K, si.F16, si.F16, config=conf)
+    assert np.array_equal(c1, c2)  # the ranges are added in a fixed order
+    check_full(a, b, K, si.F16, si.F16, c1, N)
+
+
+@pytest.mark.parametrize("M,N,K,lda,ldb", [(200, 130, 77, 77, 77), (70, 300, 3071, 3071, 3075),
+                                           (257, 33, 1, 1, 1), (64, 64, 200, 203, 200), (33, 65, 24, 25, 24)])
+def test_staged_operands_bit_exact(M, N, K, lda, ldb):
+    # K or a leading dimension not a multiple of 8 (rows only 2-byte aligned): the staged path
+    for in_dt in (si.F16, si.BF16):
+        a = ints(M, K, in_dt, M + K, ld=lda)
+        b = ints(N, K, in_dt, N + K, ld=ldb)
+        c, desc = run_gpu(a, b, K, in_dt, si.F32)
+        assert desc["load_path"] == spt.GEMM_LOAD_STAGED
+        check_full(a, b, K, in_dt, si.F32, c, N, exact=True)
+        # the same through explicit kernels, with split K and misaligned base pointers
+        for conf in (cfg(128, 128, 4, path=spt.GEMM_LOAD_STAGED), ring_cfg(64, 5, 8, path=spt.GEMM_LOAD_STAGED),
+                     cfg(64, 64, 4, path=spt.GEMM_LOAD_STAGED, splits=3)):
+            c, desc = run_gpu(a, b, K, in_dt, si.BF16, config=conf, a_off=1, b_off=3)
+            assert desc["load_path"] == spt.GEMM_LOAD_STAGED
+            check_full(a, b, K, in_dt, si.BF16, c, N, exact=True)
+
+
+def test_workspace_sizes():
+    p = spt.Plan(300, 500, 4096, torch.float16, torch.float16, config=cfg(64, 64, 4, splits=4))
+    assert p.workspace_bytes() == 4 * 300 * 504 * 4
+    p.close()
+    p = spt.Plan(300, 500, 3071, torch.float16, torch.float16)  # staged: A and B rows of 3072
+    assert p.describe()["load_path"] == spt.GEMM_LOAD_STAGED
+    assert p.workspace_bytes() >= (300 + 500) * 3072 * 2
+    p.close()
+    p = spt.Plan(4096, 4096, 4096, torch.bfloat16, torch.bfloat16)
+    assert p.workspace_bytes() == 0
+    p.close()
 
 
 # ------------------------------------------------------------------------- the workloads

@@ -83,7 +83,7 @@ WORKLOAD_SHAPES = {
 def ring_bytes(c):
     """LDS of a configuration's ring: S stages of an A and a B K-tile, or, for the split ring (bk
     64, five slots, square tile), five operand slots of one K-tile each."""
-    if c["load_path"] == spt.GEMM_LOAD_DMA and c["bk"] == 64 and c["stages"] == 5 and c["bm"] == c["bn"]:
+    if c["load_path"] != spt.GEMM_LOAD_REG and c["bk"] == 64 and c["stages"] == 5 and c["bm"] == c["bn"]:
         return 5 * c["bm"] * c["bk"] * 2
     return c["stages"] * (c["bm"] + c["bn"]) * c["bk"] * 2
 
@@ -94,17 +94,41 @@ def test_config_choice(name):
     c = spt.gemm_select_config(M, N, K, i, i, o, K, K, N, 256, 160 * 1024)
     assert c["lds_bytes"] == ring_bytes(c) <= 160 * 1024
     tiles = math.ceil(M / c["bm"]) * math.ceil(N / c["bn"])
-    assert 1 <= c["grid"] <= min(tiles, 512)
+    units = tiles * c["splits"]
+    assert 1 <= c["grid"] <= min(units, 512)
     if K % 8 == 0:
         assert c["load_path"] == spt.GEMM_LOAD_DMA
     else:
-        assert c["load_path"] == spt.GEMM_LOAD_REG  # lda = 3071: rows are only 2-byte aligned
+        # lda = 3071: rows are only 2-byte aligned, so the operands are first copied into rows of 3072
+        assert c["load_path"] == spt.GEMM_LOAD_STAGED
+    kt = math.ceil(math.ceil(K / 8) * 8 / c["bk"])
+    if c["splits"] > 1:
+        per = math.ceil(kt / c["splits"])
+        assert per >= 8 and (c["splits"] - 1) * per < kt  # every K range non-empty, none tiny
+        assert c["splits"] * M * math.ceil(N / 8) * 8 * 4 <= 1 << 30
     if name in ("c2", "c3", "c4"):
-        # the two-wave-group kernel with the split ring
+        # the two-wave-group kernel with the split ring, whole K per tile
         assert (c["bm"], c["bn"], c["bk"], c["stages"], c["waves"]) == (256, 256, 64, 5, 8) and tiles >= 256
-        assert c["lds_bytes"] == 160 * 1024
-    if name == "c5c":
-        assert tiles >= 256  # the tile menu fills every CU
+        assert c["lds_bytes"] == 160 * 1024 and c["splits"] == 1
+    if name in ("c5a", "c5c"):
+        assert units >= 256 and c["splits"] > 1  # too few tiles for 256 CUs: K is split to fill them
+    if name == "c5a":
+        assert c["bm"] == 64  # M = 32: a larger tile would be mostly padding
+
+
+def test_split_choice_small_k_and_limits():
+    # K too short to split (fewer than 16 K-tiles): one range per tile
+    c = spt.gemm_select_config(64, 64, 512, F16, F16, F16, 512, 512, 64, 256, 160 * 1024)
+    assert c["splits"] == 1
+    # K = 0: nothing to split
+    c = spt.gemm_select_config(64, 64, 0, F16, F16, F16, 8, 8, 64, 256, 160 * 1024)
+    assert c["splits"] == 1
+    # enough output tiles: no split even with a long K
+    c = spt.gemm_select_config(4096, 4096, 65536, BF16, BF16, BF16, 65536, 65536, 4096, 256, 160 * 1024)
+    assert c["splits"] == 1
+    # a large M*N with few tiles per device slot: the partial planes stay under 1 GiB
+    c = spt.gemm_select_config(2048, 2048, 1 << 20, BF16, BF16, F32, 1 << 20, 1 << 20, 2048, 256, 160 * 1024)
+    assert c["splits"] * 2048 * 2048 * 4 <= 1 << 30
 
 
 def test_config_override_validation():
@@ -115,7 +139,9 @@ def test_config_override_validation():
     bad = dict(good, bm=96)
     import ctypes
     for conf, st in ((bad, INVALID), (dict(good, stages=5), INVALID), (dict(good, mfma=32), INVALID),
-                     (dict(good, load_path=7), INVALID), (dict(good, bm=256, bn=256, stages=3), INVALID)):
+                     (dict(good, load_path=7), INVALID), (dict(good, bm=256, bn=256, stages=3), INVALID),
+                     (dict(good, splits=-1), INVALID), (dict(good, splits=17), INVALID),
+                     (dict(good, load_path=2, stages=2, splits=2), INVALID)):
         c = spt.GemmConfig.from_dict(conf)
         p = ctypes.c_void_p()
         # without a GPU plan creation stops at the device query; the override is checked after it,
@@ -126,32 +152,43 @@ def test_config_override_validation():
 
 # ------------------------------------------------------------------------------ scheduler
 
-@pytest.mark.parametrize("tiles_m,tiles_n,group_m,grid", [
-    (32, 32, 8, 256), (32, 32, 8, 148), (5, 7, 8, 6), (7, 5, 3, 16), (64, 64, 8, 256), (1, 1, 8, 1),
-    (33, 17, 8, 256), (4, 64, 8, 256), (32, 4, 8, 128), (8, 8, 1, 64), (3, 3, 2, 1000 // 100)])
-def test_schedule_covers_every_tile_once(tiles_m, tiles_n, group_m, grid):
+@pytest.mark.parametrize("tiles_m,tiles_n,splits,group_m,grid", [
+    (32, 32, 1, 8, 256), (32, 32, 1, 8, 148), (5, 7, 1, 8, 6), (7, 5, 1, 3, 16), (64, 64, 1, 8, 256),
+    (1, 1, 1, 8, 1), (33, 17, 1, 8, 256), (4, 64, 1, 8, 256), (32, 4, 1, 8, 128), (8, 8, 1, 1, 64),
+    (3, 3, 1, 2, 1000 // 100), (1, 128, 4, 8, 512), (32, 4, 2, 8, 256), (5, 7, 3, 8, 64), (1, 1, 16, 8, 7)])
+def test_schedule_covers_every_unit_once(tiles_m, tiles_n, splits, group_m, grid):
     seen = {}
     per_worker = [0] * grid
-    T = tiles_m * tiles_n
+    T = tiles_m * tiles_n * splits
     rounds = math.ceil(T / grid)
     for wg in range(grid):
         for r in range(rounds + 1):
-            t = spt.gemm_schedule_tile(tiles_m, tiles_n, group_m, grid, wg, r)
+            t = spt.gemm_schedule_tile(tiles_m, tiles_n, splits, group_m, grid, wg, r)
             if t is None:
                 continue
-            assert 0 <= t[0] < tiles_m and 0 <= t[1] < tiles_n
-            assert t not in seen, f"tile {t} assigned twice"
+            assert 0 <= t[0] < tiles_m and 0 <= t[1] < tiles_n and 0 <= t[2] < splits
+            assert t not in seen, f"unit {t} assigned twice"
             seen[t] = (wg, r)
             per_worker[wg] += 1
     assert len(seen) == T
     assert max(per_worker) == math.ceil(T / grid)
 
 
+def test_schedule_split_ranges_run_range_by_range():
+    # 8192x1024 at 256x256 with K in two ranges (128 tiles, 256 workgroups): the first round holds
+    # every tile once per range, and the workgroups of one XCD share one range
+    for x in range(8):
+        units = [spt.gemm_schedule_tile(32, 4, 2, 8, 256, wg, 0) for wg in range(x, 256, 8)]
+        assert len({u[2] for u in units}) == 1
+    first = [spt.gemm_schedule_tile(32, 4, 2, 8, 256, wg, 0) for wg in range(256)]
+    assert sorted(first) == sorted((m, n, s) for m in range(32) for n in range(4) for s in range(2))
+
+
 def test_schedule_page_example_tiles_per_worker():
     g = GOLDEN["persistent_tiles"]
     tm, tn = g["M"] // g["tile"], g["N"] // g["tile"]
     assert tm * tn == g["tiles"]
-    counts = [sum(1 for r in range(10) if spt.gemm_schedule_tile(tm, tn, 8, g["workers"], wg, r) is not None)
+    counts = [sum(1 for r in range(10) if spt.gemm_schedule_tile(tm, tn, 1, 8, g["workers"], wg, r) is not None)
               for wg in range(g["workers"])]
     assert sum(counts) == g["tiles"]
     assert max(counts) == g["tiles_per_worker_ceil"]
@@ -161,7 +198,7 @@ def test_schedule_keeps_each_xcd_on_a_compact_block():
     # 8192^3 at 256x256: 32x32 tiles, 256 workgroups; workgroup w runs on XCD w % 8.
     for r in range(4):
         for x in range(8):
-            tiles = [spt.gemm_schedule_tile(32, 32, 8, 256, wg, r) for wg in range(x, 256, 8)]
+            tiles = [spt.gemm_schedule_tile(32, 32, 1, 8, 256, wg, r) for wg in range(x, 256, 8)]
             rows = {t[0] for t in tiles}
             cols = {t[1] for t in tiles}
             assert len(tiles) == 32 and len(rows) * len(cols) == 32 and len(rows) <= 8 and len(cols) <= 4
@@ -169,9 +206,11 @@ def test_schedule_keeps_each_xcd_on_a_compact_block():
 
 def test_schedule_invalid_args():
     with pytest.raises(spt.GemmError):
-        spt.gemm_schedule_tile(0, 4, 8, 4, 0, 0)
+        spt.gemm_schedule_tile(0, 4, 1, 8, 4, 0, 0)
     with pytest.raises(spt.GemmError):
-        spt.gemm_schedule_tile(4, 4, 8, 4, 4, 0)
+        spt.gemm_schedule_tile(4, 4, 1, 8, 4, 4, 0)
+    with pytest.raises(spt.GemmError):
+        spt.gemm_schedule_tile(4, 4, 0, 8, 4, 0, 0)
 
 
 # ------------------------------------------------------------------------------ LDS layout
