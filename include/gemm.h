@@ -73,7 +73,8 @@ typedef enum {
  *   waves        wavefronts per workgroup (64 lanes each); 8 selects the two-wave-group kernel
  *                (256x256, bk 64, stages 2 or 5), where one group of four waves runs MFMAs while
  *                the other issues loads, alternating at workgroup barriers
- *   mfma         MFMA shape: 16 = v_mfma_f32_16x16x32_{f16,bf16}
+ *   mfma         MFMA shape: 16 = v_mfma_f32_16x16x32_{f16,bf16}; 32 = v_mfma_f32_32x32x16_{f16,bf16}
+ *                (two-wave-group kernel with the split ring only: 256x256, bk 64, stages 5, waves 8)
  *   persistent   1: launch min(#tiles, grid) workgroups that loop over tiles; 0: one per tile
  *   group_m      grouped raster height, in tiles (tiles sharing A row bands run back to back)
  *   load_path    gemm_load_path_t

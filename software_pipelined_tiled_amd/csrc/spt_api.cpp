@@ -86,7 +86,8 @@ bool offsets_fit(const gemm_config_t& c, int64_t lda, int64_t ldb, int64_t ldc, 
 
 const spt::KernelEntry* find_entry(const spt::KernelEntry* t, int n, const gemm_config_t& c) {
   for (int i = 0; i < n; ++i)
-    if (t[i].bm == c.bm && t[i].bn == c.bn && t[i].bk == c.bk && t[i].stages == c.stages && t[i].waves == c.waves)
+    if (t[i].bm == c.bm && t[i].bn == c.bn && t[i].bk == c.bk && t[i].stages == c.stages && t[i].waves == c.waves &&
+        t[i].mfma == c.mfma)
       return &t[i];
   return nullptr;
 }
@@ -202,7 +203,7 @@ void finish_config(gemm_config_t& c, int64_t M, int64_t N, int cu_count, int lds
 }
 
 gemm_status_t validate_override(const gemm_config_t& c) {
-  if (c.mfma != 16 && c.mfma != 0) return GEMM_ERR_INVALID;
+  if (c.mfma != 16 && c.mfma != 32 && c.mfma != 0) return GEMM_ERR_INVALID;
   if (c.load_path < GEMM_LOAD_AUTO || c.load_path > GEMM_LOAD_STAGED) return GEMM_ERR_INVALID;
   if (c.group_m < 0 || c.grid < 0) return GEMM_ERR_INVALID;
   if (c.splits < 0 || c.splits > kMaxSplits) return GEMM_ERR_INVALID;

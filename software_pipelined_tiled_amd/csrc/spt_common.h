@@ -74,6 +74,14 @@ SPT_HD int b_row_perm(int rho) {
   return base + 8 * g + 4 * h + i;
 }
 
+// The same for the 32x32 MFMA, which hands lane l the output columns 8g + 4(l/32) + e (g, e < 4) of a
+// 32-column block: within each 32-row group, LDS row 8g + 4h + i holds global row
+// 16(g/2) + 8h + 4(g mod 2) + i, so groups g = 0, 1 (and 2, 3) give a lane 8 consecutive columns.
+SPT_HD int b_row_perm32(int rho) {
+  const int base = rho & ~31, g = (rho >> 3) & 3, h = (rho >> 2) & 1, i = rho & 3;
+  return base + 16 * (g >> 1) + 8 * h + 4 * (g & 1) + i;
+}
+
 // Split-K work units. With `splits` K ranges per output tile, a launch has tiles_m * tiles_n *
 // splits work units; unit t computes K range s = t / (tiles_m * tiles_n) of output tile number
 // t mod (tiles_m * tiles_n) in the grouped raster, so units of one K range run side by side and

@@ -129,6 +129,24 @@ __device__ __forceinline__ f32x4 mfma16<_Float16>(u32x4 x, u32x4 y, f32x4 c) {
                                                 0, 0, 0);
 }
 
+// v_mfma_f32_32x32x16: D[i][j] += sum_k X[i][k] Y[j][k] over a 32x32 block and 16 k. Lane l supplies
+// row l mod 32 of X and of Y (8 values of k each; both operands use the same lane-to-k map, so the
+// pairing of products does not depend on it) and holds D[8g + 4(l/32) + e][l mod 32] in element
+// 4g + e of the result (g < 4, e < 4).
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+template <typename TIn>
+__device__ __forceinline__ f32x16 mfma32(u32x4 x, u32x4 y, f32x16 c);
+template <>
+__device__ __forceinline__ f32x16 mfma32<__bf16>(u32x4 x, u32x4 y, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, x), __builtin_bit_cast(bf16x8, y), c,
+                                                 0, 0, 0);
+}
+template <>
+__device__ __forceinline__ f32x16 mfma32<_Float16>(u32x4 x, u32x4 y, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, x), __builtin_bit_cast(f16x8, y), c,
+                                                0, 0, 0);
+}
+
 // ------------------------------------------------------------------------------ epilogue
 __device__ __forceinline__ unsigned pack_bf16(float a, float b) {
   return (unsigned)__builtin_bit_cast(unsigned short, (__bf16)a) |

@@ -350,6 +350,7 @@ static KernelEntry make_entry() {
   KernelEntry e;
   e.bm = BM; e.bn = BN; e.bk = BK; e.stages = S; e.waves = T::W; e.load_path = 1;
   e.lds_bytes = T::LDS;
+  e.mfma = 16;
   e.fn[0][0] = (const void*)&gemm_dma_kernel<BM, BN, BK, S, WM, WN, _Float16, 0>;
   e.fn[0][1] = (const void*)&gemm_dma_kernel<BM, BN, BK, S, WM, WN, _Float16, 1>;
   e.fn[0][2] = (const void*)&gemm_dma_kernel<BM, BN, BK, S, WM, WN, _Float16, 2>;

@@ -51,14 +51,19 @@ struct PpTile {
   int ks, kb;  // K range index and its first K element
 };
 
-template <int S, typename TIn, int OUT>
+// MF: the MFMA shape, 16 (v_mfma_f32_16x16x32) or 32 (v_mfma_f32_32x32x16). A fragment is MF rows of
+// the K-tile at the MFMA's depth (32 or 16 elements): 8 values per lane either way, one ds_read_b128.
+template <int S, int MF, typename TIn, int OUT>
 __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmArgs args) {
   constexpr int BM = 256, BN = 256, BK = 64;
   constexpr bool SPLIT = S == 5;
   constexpr int TM = 64, TN = 128;                   // wave tile
-  constexpr int FM = TM / 16, FN = TN / 16;          // 4 A fragments, 8 B fragments per k-step
-  constexpr int NSUB = BK / 32;                      // 2 k-steps per K-tile
-  constexpr int FRAG = 16 * 128;                     // bytes between 16-row fragments
+  constexpr int MK = MF == 16 ? 32 : 16;             // K depth of one MFMA
+  constexpr int FM = TM / MF, FN = TN / MF;          // A and B fragments per k-step (4, 8 or 2, 4)
+  constexpr int NSUB = BK / MK;                      // k-steps per K-tile (2 or 4)
+  constexpr int FRAG = MF * 128;                     // bytes between fragments
+  using Acc = std::conditional_t<MF == 16, f32x4, f32x16>;
+  static_assert(MF == 16 || MF == 32, "16x16x32 or 32x32x16 MFMA");
   constexpr int A_BYTES = BM * BK * 2, STAGE = (BM + BN) * BK * 2;
   constexpr int LDS = SPLIT ? S * A_BYTES : S * STAGE;
   constexpr int LA = A_BYTES / 1024 / 4, LB = LA;    // DMA instructions per wave for one operand tile
@@ -100,8 +105,8 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmArgs args) {
     for (int t = u0; t < args.num_tiles; t += args.grid) {
       const PpTile tl = tile_at(t);
       const __amdgpu_buffer_rsrc_t rc = c_rsrc(tl);
-      for (int pu = 0; pu < FN / 2; ++pu)
-        for (int j = 0; j < FM; ++j)
+      for (int pu = 0; pu < TN / 32; ++pu)
+        for (int j = 0; j < TM / 16; ++j)
           store8<OUT, true>(z, rc, m_base + 16 * j + (lane & 15), tl.rows_left,
                             tl.col0 + TN * wn + 32 * pu + 8 * (lane >> 4), N, args.ldc);
     }
@@ -111,19 +116,22 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmArgs args) {
   // DMA. Wave v's instruction j of an operand tile fills LDS rows 8q .. 8q+7 (q = LA*v + j) of the
   // tile; lane l lands at row 8q + l/8, physical chunk l%8, which holds logical chunk (l%8) XOR
   // swz(l/8) (the swizzle has period 8 in the row, so it depends on the lane alone). The row
-  // splits into a wave-uniform part 8q and a lane part l/8; B rows are staged permuted, and
-  // b_row_perm splits the same way (it permutes within aligned 32-row groups).
+  // splits into a wave-uniform part 8q and a lane part l/8; B rows are staged permuted, and both
+  // permutations split the same way (they permute within aligned 32-row groups, and rows 8q .. 8q+7
+  // keep their offsets 8(r/4) + r%4 relative to the image of 8q).
+  auto bperm = [](int rho) SPT_INLINE { return MF == 16 ? b_row_perm(rho) : b_row_perm32(rho); };
   const int lrow = lane >> 3;
   const int lane_kc = 8 * ((lane & 7) ^ swz(lrow));
-  const int a_lrow = lrow, b_lrow = b_row_perm(lrow);
+  const int a_lrow = lrow, b_lrow = bperm(lrow);
   auto a_urow = [&](int j) SPT_INLINE { return 8 * (LA * v + j); };
-  auto b_urow = [&](int j) SPT_INLINE { return b_row_perm(8 * (LB * v + j)); };
-  // fragment read offsets inside an operand tile, k-step s (fragment f adds 16 rows)
+  auto b_urow = [&](int j) SPT_INLINE { return bperm(8 * (LB * v + j)); };
+  // fragment read offsets inside an operand tile, k-step s (fragment f adds MF rows): lane l reads
+  // row l mod MF, the 8-element chunk l / MF of the k-step's MK elements
   int a_rd[NSUB], b_rd[NSUB];
 #pragma unroll
   for (int s = 0; s < NSUB; ++s) {
-    a_rd[s] = lds_chunk_offset(BM, 128 * grp + TM * wm + (lane & 15), 4 * s + (lane >> 4));
-    b_rd[s] = lds_chunk_offset(BN, TN * wn + (lane & 15), 4 * s + (lane >> 4));
+    a_rd[s] = lds_chunk_offset(BM, 128 * grp + TM * wm + lane % MF, (MK / 8) * s + lane / MF);
+    b_rd[s] = lds_chunk_offset(BN, TN * wn + lane % MF, (MK / 8) * s + lane / MF);
   }
 
   // A position in the K-tile stream: an output tile and a K-tile inside it. advance() moves to the
@@ -185,8 +193,10 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmArgs args) {
   };
 
   u32x4 xf[NSUB][FN], yf[NSUB][FM];  // the K-tile's fragments: B side (x), A side (y)
-  f32x4 acc[FN][FM];
-  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  Acc acc[FN][FM];
+  Acc zero_acc;
+#pragma unroll
+  for (int e = 0; e < (int)(sizeof(Acc) / sizeof(float)); ++e) zero_acc[e] = 0.f;
 
   auto read_frags = [&](int p) SPT_INLINE {
     const int pu = __builtin_amdgcn_readfirstlane(p);
@@ -209,7 +219,8 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmArgs args) {
       constexpr int s = decltype(s_c)::value;
       static_for<FN * FM>([&](auto m_c) {
         constexpr int m = decltype(m_c)::value, i = m / FM, j = m % FM;
-        acc[i][j] = mfma16<TIn>(xf[s][i], yf[s][j], (kFirst && s == 0) ? zero4 : acc[i][j]);
+        if constexpr (MF == 16) acc[i][j] = mfma16<TIn>(xf[s][i], yf[s][j], (kFirst && s == 0) ? zero_acc : acc[i][j]);
+        else acc[i][j] = mfma32<TIn>(xf[s][i], yf[s][j], (kFirst && s == 0) ? zero_acc : acc[i][j]);
       });
     });
     __builtin_amdgcn_sched_barrier(0);
@@ -229,22 +240,44 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmArgs args) {
     tl.kb = 0;
     const __amdgpu_buffer_rsrc_t rc = c_rsrc(tl);
     const int ln = (int)opaque_u32((unsigned)lane);
-    const int m_lane = m_base + (ln & 15), n_lane = tl.col0 + TN * wn + 8 * (ln >> 4);
+    const int m_lane = m_base + ln % MF, n_lane = tl.col0 + TN * wn + 8 * (ln / MF);
     const bool full = tl.rows_left >= BM && tl.cols_left >= BN;
     const unsigned voff = (unsigned)(m_lane * args.ldc + n_lane) * (unsigned)es;
+    // 8 consecutive outputs at (m_lane + dm, n_lane + dn)
+    auto put8 = [&](const float (&vv)[8], int dm, int dn) SPT_INLINE {
+      if (full) store8_at<OUT>(vv, rc, voff, (unsigned)((dm * args.ldc + dn) * es));
+      else store8<OUT, true>(vv, rc, m_lane + dm, tl.rows_left, n_lane + dn, N, args.ldc);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    if constexpr (MF == 16) {
+      // B fragments 2pu and 2pu+1 hold columns 32pu + 8(l/16) + 0..3 and + 4..7
 #pragma unroll
-    for (int pu = 0; pu < FN / 2; ++pu) {
+      for (int pu = 0; pu < FN / 2; ++pu) {
 #pragma unroll
-      for (int j = 0; j < FM; ++j) {
-        float vv[8];
+        for (int j = 0; j < FM; ++j) {
+          float vv[8];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          vv[e] = acc[2 * pu][j][e];
-          vv[4 + e] = acc[2 * pu + 1][j][e];
+          for (int e = 0; e < 4; ++e) {
+            vv[e] = acc[2 * pu][j][e];
+            vv[4 + e] = acc[2 * pu + 1][j][e];
+          }
+          put8(vv, 16 * j, 32 * pu);
         }
-        if (full) store8_at<OUT>(vv, rc, voff, (unsigned)((16 * j * args.ldc + 32 * pu) * es));
-        else store8<OUT, true>(vv, rc, m_lane + 16 * j, tl.rows_left, n_lane + 32 * pu, N, args.ldc);
-        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      // elements 8h .. 8h+7 of a block hold columns 32i + 16h + 8(l/32) + 0..7
+#pragma unroll
+      for (int i = 0; i < FN; ++i) {
+#pragma unroll
+        for (int j = 0; j < FM; ++j) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            float vv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) vv[e] = acc[i][j][8 * h + e];
+            put8(vv, 32 * j, 32 * i + 16 * h);
+          }
+        }
       }
     }
   };
@@ -348,22 +381,23 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmArgs args) {
   }
 }
 
-template <int S>
+template <int S, int MF>
 static KernelEntry make_pp_entry() {
   KernelEntry k;
   k.bm = 256; k.bn = 256; k.bk = 64; k.stages = S; k.waves = 8; k.load_path = 1;
   k.lds_bytes = S == 5 ? 5 * 256 * 64 * 2 : S * (256 + 256) * 64 * 2;
-  k.fn[0][0] = (const void*)&gemm_pp_kernel<S, _Float16, 0>;
-  k.fn[0][1] = (const void*)&gemm_pp_kernel<S, _Float16, 1>;
-  k.fn[0][2] = (const void*)&gemm_pp_kernel<S, _Float16, 2>;
-  k.fn[1][0] = (const void*)&gemm_pp_kernel<S, __bf16, 0>;
-  k.fn[1][1] = (const void*)&gemm_pp_kernel<S, __bf16, 1>;
-  k.fn[1][2] = (const void*)&gemm_pp_kernel<S, __bf16, 2>;
+  k.mfma = MF;
+  k.fn[0][0] = (const void*)&gemm_pp_kernel<S, MF, _Float16, 0>;
+  k.fn[0][1] = (const void*)&gemm_pp_kernel<S, MF, _Float16, 1>;
+  k.fn[0][2] = (const void*)&gemm_pp_kernel<S, MF, _Float16, 2>;
+  k.fn[1][0] = (const void*)&gemm_pp_kernel<S, MF, __bf16, 0>;
+  k.fn[1][1] = (const void*)&gemm_pp_kernel<S, MF, __bf16, 1>;
+  k.fn[1][2] = (const void*)&gemm_pp_kernel<S, MF, __bf16, 2>;
   return k;
 }
 
 const KernelEntry* pp_kernel_table(int* count) {
-  static const KernelEntry table[] = {make_pp_entry<5>(), make_pp_entry<2>()};
+  static const KernelEntry table[] = {make_pp_entry<5, 16>(), make_pp_entry<2, 16>(), make_pp_entry<5, 32>()};
   *count = (int)(sizeof(table) / sizeof(table[0]));
   return table;
 }

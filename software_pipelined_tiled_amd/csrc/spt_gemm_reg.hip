@@ -182,6 +182,7 @@ static KernelEntry make_reg_entry() {
   KernelEntry e;
   e.bm = BM; e.bn = BN; e.bk = BK; e.stages = 2; e.waves = T::W; e.load_path = 2;
   e.lds_bytes = T::LDS;
+  e.mfma = 16;
   e.fn[0][0] = (const void*)&gemm_reg_kernel<BM, BN, BK, WM, WN, _Float16, 0>;
   e.fn[0][1] = (const void*)&gemm_reg_kernel<BM, BN, BK, WM, WN, _Float16, 1>;
   e.fn[0][2] = (const void*)&gemm_reg_kernel<BM, BN, BK, WM, WN, _Float16, 2>;

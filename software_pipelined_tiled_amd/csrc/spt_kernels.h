@@ -6,6 +6,7 @@ namespace spt {
 struct KernelEntry {
   int bm, bn, bk, stages, waves, load_path;  // load_path: 1 = DMA, 2 = REG
   int lds_bytes;
+  int mfma;  // 16: v_mfma_f32_16x16x32, 32: v_mfma_f32_32x32x16
   const void* fn[2][3];  // __global__ void(GemmArgs), by [input f16/bf16][output f16/bf16/f32]
 };
 

@@ -57,7 +57,7 @@ def kernel_source_hash() -> str:
 def kernel_prefix(plan: dict) -> str:
     """Start of the demangled template name of the kernel a plan launches."""
     if plan["load_path"] != 2 and plan["waves"] == 8:
-        return f"gemm_pp_kernel<{plan['stages']}, "
+        return f"gemm_pp_kernel<{plan['stages']}, {plan.get('mfma', 16)}, "
     kind = "reg" if plan["load_path"] == 2 else "dma"
     return f"gemm_{kind}_kernel<{plan['bm']}, {plan['bn']}, {plan['bk']}, "
 
@@ -70,6 +70,7 @@ def kernel_label(plan: dict, in_dt: str, out_dt: str) -> str:
     out = "f32" if splits > 1 else out_dt
     extra = f",splits={splits}" if splits > 1 else ""
     extra += ",staged" if plan["load_path"] == 3 else ""
+    extra += ",mfma32x32x16" if plan.get("mfma", 16) == 32 else ""
     return (f"gemm_{kind}_kernel<{plan['bm']},{plan['bn']},{plan['bk']},{plan['stages']},"
             f"waves={plan['waves']},{in_dt},{out}{extra}>")
 

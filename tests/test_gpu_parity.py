@@ -36,8 +36,8 @@ REG_CONFIGS = [(128, 128, 2), (64, 64, 2)]
 RING_CONFIGS = [(64, 5, 4), (32, 4, 4), (64, 5, 8), (64, 2, 8)]
 
 
-def cfg(bm, bn, s, path=spt.GEMM_LOAD_DMA, persistent=1, group_m=8, grid=0, bk=64, waves=4, splits=1):
-    return dict(bm=bm, bn=bn, bk=bk, stages=s, waves=waves, mfma=16, persistent=persistent, group_m=group_m,
+def cfg(bm, bn, s, path=spt.GEMM_LOAD_DMA, persistent=1, group_m=8, grid=0, bk=64, waves=4, splits=1, mfma=16):
+    return dict(bm=bm, bn=bn, bk=bk, stages=s, waves=waves, mfma=mfma, persistent=persistent, group_m=group_m,
                 load_path=path, grid=grid, lds_bytes=0, splits=splits)
 
 
@@ -111,7 +111,8 @@ def test_output_dtypes_bit_exact(in_dt, out_dt):
     a = ints(M, K, in_dt, 7)
     b = ints(N, K, in_dt, 8)
     for c_cfg in (cfg(256, 256, 2), cfg(128, 128, 4), cfg(128, 128, 2, path=spt.GEMM_LOAD_REG),
-                  ring_cfg(64, 5, 8), ring_cfg(64, 5, 4), ring_cfg(64, 5, 8, splits=3), cfg(64, 64, 4, splits=2)):
+                  ring_cfg(64, 5, 8), ring_cfg(64, 5, 4), ring_cfg(64, 5, 8, splits=3), cfg(64, 64, 4, splits=2),
+                  ring_cfg(64, 5, 8, mfma=32)):
         c, _ = run_gpu(a, b, K, in_dt, out_dt, config=c_cfg)
         check_full(a, b, K, in_dt, out_dt, c, N, exact=True)
 
@@ -178,6 +179,34 @@ def test_deterministic_and_grouping_invariant():
     c3, _ = run_gpu(a, b, K, si.BF16, si.BF16, config=cfg(128, 128, 4, group_m=1, persistent=0))
     assert np.array_equal(c1, c2) and np.array_equal(c1, c3)  # tile order does not change any sum
     check_full(a, b, K, si.BF16, si.BF16, c1, N)
+
+
+# ------------------------------------------------------------------------- 32x32x16 MFMA
+
+@pytest.mark.parametrize("persistent", [1, 0])
+@pytest.mark.parametrize("M,N,K", [(256 + 131, 512 - 37, 7 * 64 + 24), (256, 256, 64), (1, 300, 8), (513, 257, 520)])
+def test_mfma32_bit_exact(M, N, K, persistent):
+    # the two-group kernel on v_mfma_f32_32x32x16: its own fragment rows, B-row order and epilogue
+    for in_dt in (si.F16, si.BF16):
+        a = ints(M, K, in_dt, 1100 + M + K)
+        b = ints(N, K, in_dt, 1200 + N + K)
+        for out_dt in (si.F32, si.BF16):
+            c, desc = run_gpu(a, b, K, in_dt, out_dt,
+                              config=ring_cfg(64, 5, 8, mfma=32, persistent=persistent, grid=3 if persistent else 0))
+            assert desc["mfma"] == 32
+            check_full(a, b, K, in_dt, out_dt, c, N, exact=True)
+
+
+def test_mfma32_split_k_and_real_values():
+    M, N, K = 300, 700, 4096
+    a = ints(M, K, si.BF16, 1301)
+    b = ints(N, K, si.BF16, 1302)
+    c, _ = run_gpu(a, b, K, si.BF16, si.F32, config=ring_cfg(64, 5, 8, mfma=32, splits=3))
+    check_full(a, b, K, si.BF16, si.F32, c, N, exact=True)
+    a = si.make_matrix(M, K, si.BF16, "normal_scaled", 1303, k_for_scale=K)
+    b = si.make_matrix(N, K, si.BF16, "normal_scaled", 1304, k_for_scale=K)
+    c, _ = run_gpu(a, b, K, si.BF16, si.BF16, config=ring_cfg(64, 5, 8, mfma=32))
+    check_full(a, b, K, si.BF16, si.BF16, c, N)
 
 
 # ------------------------------------------------------------------------- split-K and staging
@@ -301,3 +330,5 @@ def test_workload_c1_small_full_through_each_dma_config():
     for bk, s, waves in RING_CONFIGS:
         c, _ = run_gpu(a, b, k, i_dt, o_dt, config=ring_cfg(bk, s, waves))
         check_full(a, b, k, i_dt, o_dt, c, n)
+    c, _ = run_gpu(a, b, k, i_dt, o_dt, config=ring_cfg(64, 5, 8, mfma=32))
+    check_full(a, b, k, i_dt, o_dt, c, n)
