@@ -5,7 +5,13 @@ Default workload: M = N = K = 8192, bf16 inputs drawn N(0,1)/sqrt(K), fp32 accum
 output. One step is one gemm_run over operands already resident in HBM. Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--shape-index I]
-                    [--config JSON] [--no-cpu-baseline] [--copy-calibration]
+                    [--config JSON] [--no-cpu-baseline] [--copy-calibration] [--cold]
+
+The roofline object names the bound of the workload: "mfma" (TFLOP/s against the dense peak) when
+2MNK at the MFMA peak takes longer than the compulsory bytes at 8 TB/s, else "hbm" (compulsory GB/s
+against 8 TB/s). A plan that splits K or stages its operands launches more than one kernel per run;
+the per-launch time is then that of the whole run (mainloop plus reduction or staging copy).
+With --cold, B rotates over enough copies that the 256 MB MALL cannot hold them, so B comes from HBM.
 """
 from __future__ import annotations
 
@@ -77,6 +83,7 @@ def main() -> int:
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also launch one 1 GiB copy kernel (reference for memory-traffic counters)")
     ap.add_argument("--no-probes", action="store_true", help="skip the MFMA-peak and HBM-copy probes")
+    ap.add_argument("--cold", action="store_true", help="rotate B over copies that together exceed the MALL")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -97,14 +104,18 @@ def main() -> int:
     A = torch.from_numpy(a_bits.view(np.int16)).cuda().view(tdt[in_dt])
     B = torch.from_numpy(b_bits.view(np.int16)).cuda().view(tdt[in_dt])
     C = torch.empty((M, N), dtype=tdt[out_dt], device="cuda")
+    b_copies = [B]
+    if args.cold:  # >= 600 MB of B copies: more than the 256 MB MALL and the 8 x 4 MB of L2
+        n_copies = max(2, -(-600_000_000 // max(1, B.numel() * 2)))
+        b_copies += [B.clone() for _ in range(n_copies - 1)]
     config = json.loads(args.config) if args.config else None
     plan = spt.Plan(M, N, K, tdt[in_dt], tdt[out_dt], config=config)
     desc = plan.describe()
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
 
-    for _ in range(args.warmup):
-        plan.run_ptrs(A.data_ptr(), B.data_ptr(), C.data_ptr(), sp)
+    for i in range(args.warmup):
+        plan.run_ptrs(A.data_ptr(), b_copies[i % len(b_copies)].data_ptr(), C.data_ptr(), sp)
     torch.cuda.synchronize()
 
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
@@ -115,7 +126,7 @@ def main() -> int:
     all_start.record(stream)
     for i in range(args.steps):
         starts[i].record(stream)
-        plan.run_ptrs(A.data_ptr(), B.data_ptr(), C.data_ptr(), sp)
+        plan.run_ptrs(A.data_ptr(), b_copies[i % len(b_copies)].data_ptr(), C.data_ptr(), sp)
         ends[i].record(stream)
     all_end.record(stream)
     torch.cuda.synchronize()
@@ -130,11 +141,14 @@ def main() -> int:
     kernel_name = kernel_label(desc, DTYPE_NAME[in_dt], DTYPE_NAME[out_dt])
     traffic = load_traffic(args.workload, args.shape_index, kernel_name)
     compulsory = (M * K + N * K) * 2 + M * N * (4 if out_dt == 2 else 2)
+    hbm_bound = compulsory / (PEAK_HBM_GBS * 1e9) > flop / (PEAK_TFLOPS * 1e12)
 
     extra = {"avg_launch_ms": avg_launch_ms, "min_launch_ms": float(np.min(launch_ms)),
              "max_launch_ms": float(np.max(launch_ms)), "wall_s": wall,
              "pct_of_spec_peak": 100.0 * value / PEAK_TFLOPS,
              "compulsory_hbm_GBps": compulsory / (avg_launch_ms * 1e-3) / 1e9,
+             "mfma_achieved_TFLOPs": achieved, "cold_b_copies": len(b_copies) if args.cold else 0,
+             "workspace_bytes": plan.workspace_bytes(),
              "kernel_source_sha": kernel_source_hash()}
 
     if not args.no_probes:
@@ -174,9 +188,13 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": args.workload, "M": M, "N": N, "K": K, "in_dtype": DTYPE_NAME[in_dt],
                    "out_dtype": DTYPE_NAME[out_dt], "accumulate": "f32",
-                   "distribution": si.WORKLOADS[args.workload]["dist"], "kernel": kernel_name, "plan": desc},
-        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_TFLOPS, "traffic": traffic},
+                   "distribution": si.WORKLOADS[args.workload]["dist"], "kernel": kernel_name, "plan": desc,
+                   "b_cache": "cold (rotated copies)" if args.cold else "warm"},
+        "roofline": ({"bound": "hbm", "achieved": compulsory / (avg_launch_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
+                      "unit": "GB/s", "frac": compulsory / (avg_launch_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                      "traffic": traffic} if hbm_bound else
+                     {"bound": "mfma", "achieved": achieved, "peak": PEAK_TFLOPS, "unit": "TFLOP/s",
+                      "frac": achieved / PEAK_TFLOPS, "traffic": traffic}),
         "extra": extra,
     }
     if not args.no_cpu_baseline:

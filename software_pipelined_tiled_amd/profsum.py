@@ -55,11 +55,22 @@ def kernel_source_hash() -> str:
 
 
 def kernel_prefix(plan: dict) -> str:
-    """Start of the demangled template name of the kernel a plan launches."""
+    """Start of the demangled template name of the mainloop kernel a plan launches."""
     if plan["load_path"] != 2 and plan["waves"] == 8:
         return f"gemm_pp_kernel<{plan['stages']}, {plan.get('mfma', 16)}, "
     kind = "reg" if plan["load_path"] == 2 else "dma"
     return f"gemm_{kind}_kernel<{plan['bm']}, {plan['bn']}, {plan['bk']}, "
+
+
+def kernel_matches(plan: dict, name: str) -> bool:
+    """Whether a profiler kernel name (demangled, or left mangled as rocprofv3 does for some
+    _Float16 instantiations) is the plan's mainloop kernel."""
+    pre = kernel_prefix(plan)
+    if pre in name:
+        return True
+    base, args = pre.split("<")
+    mangled = base + "I" + "".join(f"Li{a.strip()}E" for a in args.split(",") if a.strip())
+    return mangled in name
 
 
 def kernel_label(plan: dict, in_dt: str, out_dt: str) -> str:
@@ -92,7 +103,6 @@ def kernel_stats(stats_csv: str, bench_json: str, out_md: str, command: str) -> 
     line = _bench_line(bench_json)
     plan = line["config"]["plan"]
     rows = _rows(stats_csv)
-    pre = kernel_prefix(plan)
     out = [f"# Kernel durations: {line['config']['workload']} ({line['config']['M']}x{line['config']['N']}x"
            f"{line['config']['K']}, {line['config']['in_dtype']} -> {line['config']['out_dtype']})", "",
            f"Command: `{command}`", "",
@@ -100,25 +110,32 @@ def kernel_stats(stats_csv: str, bench_json: str, out_md: str, command: str) -> 
            "| kernel | calls | average (us) | min (us) | max (us) | share of GPU time |",
            "|---|---|---|---|---|---|"]
     gemm_avg = None
+    aux = {}  # the other kernels of one gemm_run: split-K reduction, operand staging copy
     for r in rows:
         name = r.get("Name", r.get("KernelName", "?"))
         avg = float(r["AverageNs"]) / 1e3
         out.append(f"| `{name[:110]}` | {r['Calls']} | {avg:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
                    f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
-        if pre in name:
+        if kernel_matches(plan, name):
             gemm_avg = avg
+        for k in ("splitk_reduce_kernel", "stage_kernel"):
+            if k in name:
+                aux[k] = avg
     ev_us = line["extra"]["avg_launch_ms"] * 1e3
-    out += ["", f"GEMM launch time from HIP events in the same run: {ev_us:.1f} us "
-                f"(rocprofv3 average {gemm_avg:.1f} us, ratio {ev_us / gemm_avg:.3f})." if gemm_avg else
-            f"GEMM launch time from HIP events: {ev_us:.1f} us (kernel not found in the stats).",
+    run_avg = (gemm_avg or 0.0) + sum(aux.values())
+    parts = " + ".join([f"mainloop {gemm_avg:.1f}"] + [f"{k} {v:.1f}" for k, v in aux.items()]) if gemm_avg else ""
+    ro = line["roofline"]
+    out += ["", f"gemm_run time from HIP events in the same run: {ev_us:.1f} us (rocprofv3 average "
+                f"{parts} = {run_avg:.1f} us, ratio {ev_us / run_avg:.3f})." if gemm_avg else
+            f"gemm_run time from HIP events: {ev_us:.1f} us (kernel not found in the stats).",
             f"Throughput reported by bench.py in this run: {line['value']:.1f} TFLOP/s "
-            f"(roofline.achieved {line['roofline']['achieved']:.1f} TFLOP/s, frac {line['roofline']['frac']:.3f})."]
+            f"(roofline bound {ro['bound']}: achieved {ro['achieved']:.1f} {ro['unit']}, frac {ro['frac']:.3f})."]
     with open(out_md, "w") as f:
         f.write("\n".join(out) + "\n")
     print("\n".join(out))
 
 
-def _counter_means(path: str, counter: str, pre: str) -> tuple[float, float, int]:
+def _counter_means(path: str, counter: str, plan: dict) -> tuple[float, float, int]:
     """Mean per-dispatch value (bytes) of `counter` for the GEMM (skipping its first, cold launch)
     and for the copy kernel."""
     gemm, copy = [], []
@@ -126,7 +143,7 @@ def _counter_means(path: str, counter: str, pre: str) -> tuple[float, float, int
         if r["Counter_Name"] != counter:
             continue
         v = float(r["Counter_Value"]) * 1024.0  # rocprofv3 reports these two counters in KiB
-        if pre in r["Kernel_Name"]:
+        if kernel_matches(plan, r["Kernel_Name"]):
             gemm.append(v)
         elif "copy16_kernel" in r["Kernel_Name"]:
             copy.append(v)
@@ -138,9 +155,8 @@ def _counter_means(path: str, counter: str, pre: str) -> tuple[float, float, int
 def traffic(fetch_csv: str, write_csv: str, bench_json: str, out_json: str, command: str) -> None:
     line = _bench_line(bench_json)
     plan = line["config"]["plan"]
-    pre = kernel_prefix(plan)
-    f_gemm, f_copy, nf = _counter_means(fetch_csv, "FETCH_SIZE", pre)
-    w_gemm, w_copy, nw = _counter_means(write_csv, "WRITE_SIZE", pre)
+    f_gemm, f_copy, nf = _counter_means(fetch_csv, "FETCH_SIZE", plan)
+    w_gemm, w_copy, nw = _counter_means(write_csv, "WRITE_SIZE", plan)
     f_scale, w_scale = COPY_BYTES / f_copy, COPY_BYTES / w_copy
     c = line["config"]
     out_bytes = 4 if c["out_dtype"] == "f32" else 2
@@ -161,13 +177,12 @@ def traffic(fetch_csv: str, write_csv: str, bench_json: str, out_json: str, comm
 def clock(counter_csv: str, agent_csv: str, bench_json: str, out_md: str, command: str) -> None:
     line = _bench_line(bench_json)
     c = line["config"]
-    pre = kernel_prefix(c["plan"])
     gpu = next(r for r in _rows(agent_csv) if r.get("Agent_Type") == "GPU")
     n_se, n_cu = int(gpu["Num_Shader_Banks"]), int(gpu["Cu_Count"])
     fmax = float(gpu["Max_Engine_Clk_Fcompute"]) * 1e6
     per = {}
     for r in _rows(counter_csv):
-        if pre not in r["Kernel_Name"]:
+        if not kernel_matches(c["plan"], r["Kernel_Name"]):
             continue
         d = per.setdefault(int(r["Dispatch_Id"]), {"dur": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9})
         d[r["Counter_Name"]] = float(r["Counter_Value"])
