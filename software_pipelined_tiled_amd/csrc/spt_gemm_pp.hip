@@ -38,6 +38,12 @@
 // phase 2g+1 (into the slot B(g-1) left) and waits for it two phases later, with A(g+3) possibly
 // still in flight. The kernel starts by loading A(0), B(0) and A(1). Each load has two (B) or three
 // (A) phases to land, and the CU's fill path is busy in every phase.
+//
+// Inside a memory phase the eight loads are spread between the 24 fragment reads (one load, then
+// three reads). A wave issues direct global->LDS loads at about one 1 KiB instruction per 80
+// cycles however many are in flight, so eight loads occupy some 640 cycles of the phase; issued
+// as one burst they held the reads behind them and the memory phase outlasted the 64 MFMAs of
+// the other group. Interleaved, the LDS serves the reads while the loads issue.
 #include "spt_device.h"
 #include "spt_kernels.h"
 
@@ -159,29 +165,52 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmArgs args) {
   // `dst`. The lane's offset is its row times ld plus its chunk; a row past the matrix edge then
   // lies at or beyond the descriptor's num_records and reads zero. A chunk at or past K is moved
   // beyond num_records explicitly (one select per call); the K offset rides in the scalar offset.
-  auto issue_a = [&](const Cursor& c, int dst) SPT_INLINE {
-    const int k0 = __builtin_amdgcn_readfirstlane(c.u) * BK + __builtin_amdgcn_readfirstlane(c.tl.kb);
+  // An operand tile's loads, prepared once (descriptor, the lane's offset, the LDS base) and then
+  // issued one instruction at a time, so that a memory phase can spread them between its
+  // fragment reads.
+  struct OpLoads {
+    __amdgpu_buffer_rsrc_t r;
+    unsigned v0, lds;
+    int k0, ld;
+  };
+  auto prep_a = [&](const Cursor& c, int dst) SPT_INLINE {
+    OpLoads o;
+    o.k0 = __builtin_amdgcn_readfirstlane(c.u) * BK + __builtin_amdgcn_readfirstlane(c.tl.kb);
     const int row0 = __builtin_amdgcn_readfirstlane(c.tl.row0);
     const int rows_left = __builtin_amdgcn_readfirstlane(c.tl.rows_left);
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc((const char*)args.A + (size_t)row0 * args.lda * 2,
-                                                ((uint64_t)(rows_left - 1) * args.lda + K) * 2);
-    const unsigned a0 = lane_kc < K - k0 ? (unsigned)(a_lrow * args.lda + lane_kc) * 2u : kOOB;
-    const unsigned sa = smem_base + (unsigned)__builtin_amdgcn_readfirstlane(dst) + LA * v * 1024;
-#pragma unroll
-    for (int j = 0; j < LA; ++j)
-      dma16_unseen(ra, sa + j * 1024, add_in_place(a0, (unsigned)(a_urow(j) * args.lda) * 2u), 2u * k0);
+    o.r = make_rsrc((const char*)args.A + (size_t)row0 * args.lda * 2, ((uint64_t)(rows_left - 1) * args.lda + K) * 2);
+    o.v0 = lane_kc < K - o.k0 ? (unsigned)(a_lrow * args.lda + lane_kc) * 2u : kOOB;
+    o.lds = smem_base + (unsigned)__builtin_amdgcn_readfirstlane(dst) + LA * v * 1024;
+    o.ld = args.lda;
+    return o;
   };
-  auto issue_b = [&](const Cursor& c, int dst) SPT_INLINE {
-    const int k0 = __builtin_amdgcn_readfirstlane(c.u) * BK + __builtin_amdgcn_readfirstlane(c.tl.kb);
+  auto prep_b = [&](const Cursor& c, int dst) SPT_INLINE {
+    OpLoads o;
+    o.k0 = __builtin_amdgcn_readfirstlane(c.u) * BK + __builtin_amdgcn_readfirstlane(c.tl.kb);
     const int col0 = __builtin_amdgcn_readfirstlane(c.tl.col0);
     const int cols_left = __builtin_amdgcn_readfirstlane(c.tl.cols_left);
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc((const char*)args.B + (size_t)col0 * args.ldb * 2,
-                                                ((uint64_t)(cols_left - 1) * args.ldb + K) * 2);
-    const unsigned b0 = lane_kc < K - k0 ? (unsigned)(b_lrow * args.ldb + lane_kc) * 2u : kOOB;
-    const unsigned sb = smem_base + (unsigned)__builtin_amdgcn_readfirstlane(dst) + LB * v * 1024;
+    o.r = make_rsrc((const char*)args.B + (size_t)col0 * args.ldb * 2, ((uint64_t)(cols_left - 1) * args.ldb + K) * 2);
+    o.v0 = lane_kc < K - o.k0 ? (unsigned)(b_lrow * args.ldb + lane_kc) * 2u : kOOB;
+    o.lds = smem_base + (unsigned)__builtin_amdgcn_readfirstlane(dst) + LB * v * 1024;
+    o.ld = args.ldb;
+    return o;
+  };
+  // load j (< LA) of this wave's share of an A tile / a B tile
+  auto load_a = [&](const OpLoads& o, int j) SPT_INLINE {
+    dma16_unseen(o.r, o.lds + j * 1024, add_in_place(o.v0, (unsigned)(a_urow(j) * o.ld) * 2u), 2u * o.k0);
+  };
+  auto load_b = [&](const OpLoads& o, int j) SPT_INLINE {
+    dma16_unseen(o.r, o.lds + j * 1024, add_in_place(o.v0, (unsigned)(b_urow(j) * o.ld) * 2u), 2u * o.k0);
+  };
+  auto issue_a = [&](const Cursor& c, int dst) SPT_INLINE {
+    const OpLoads o = prep_a(c, dst);
 #pragma unroll
-    for (int j = 0; j < LB; ++j)
-      dma16_unseen(rb, sb + j * 1024, add_in_place(b0, (unsigned)(b_urow(j) * args.ldb) * 2u), 2u * k0);
+    for (int j = 0; j < LA; ++j) load_a(o, j);
+  };
+  auto issue_b = [&](const Cursor& c, int dst) SPT_INLINE {
+    const OpLoads o = prep_b(c, dst);
+#pragma unroll
+    for (int j = 0; j < LB; ++j) load_b(o, j);
   };
   // LDS byte offsets of the A and B tiles of K-tile g, from ring position p = 2g mod 5 (split) or
   // g mod 2 (stages)
@@ -198,17 +227,41 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmArgs args) {
 #pragma unroll
   for (int e = 0; e < (int)(sizeof(Acc) / sizeof(float)); ++e) zero_acc[e] = 0.f;
 
-  auto read_frags = [&](int p) SPT_INLINE {
+  // The K-tile's fragment reads in a fixed order (k-step s: the FN B fragments, then the FM A
+  // fragments); read i of NR.
+  constexpr int NR = NSUB * (FN + FM);
+  auto frag_bases = [&](int p, const char*& pa, const char*& pb) SPT_INLINE {
     const int pu = __builtin_amdgcn_readfirstlane(p);
-    const char* pa = smem + opaque_s32(a_at(pu));
-    const char* pb = smem + opaque_s32(b_at(pu));
-#pragma unroll
-    for (int s = 0; s < NSUB; ++s) {
-#pragma unroll
-      for (int f = 0; f < FN; ++f) xf[s][f] = *(const u32x4*)(pb + b_rd[s] + f * FRAG);
-#pragma unroll
-      for (int f = 0; f < FM; ++f) yf[s][f] = *(const u32x4*)(pa + a_rd[s] + f * FRAG);
-    }
+    pa = smem + opaque_s32(a_at(pu));
+    pb = smem + opaque_s32(b_at(pu));
+  };
+  auto read_one = [&](auto i_c, const char* pa, const char* pb) SPT_INLINE {
+    constexpr int i = decltype(i_c)::value, s = i / (FN + FM), f = i % (FN + FM);
+    if constexpr (f < FN) xf[s][f] = *(const u32x4*)(pb + b_rd[s] + f * FRAG);
+    else yf[s][f - FN] = *(const u32x4*)(pa + a_rd[s] + (f - FN) * FRAG);
+  };
+  auto read_frags = [&](int p) SPT_INLINE {
+    const char *pa, *pb;
+    frag_bases(p, pa, pb);
+    static_for<NR>([&](auto i_c) { read_one(i_c, pa, pb); });
+    wait_lgkmcnt0();
+  };
+  // The same reads with NL loads spread evenly between them: load l goes out just before read
+  // floor(l * NR / NL). A wave issues its LDS-DMA loads at a limited rate, so in a burst the
+  // reads queued behind them would wait; interleaved, the LDS serves the reads while the loads
+  // issue.
+  auto read_frags_with_loads = [&](int p, auto nl_c, auto&& load) SPT_INLINE {
+    constexpr int NL = decltype(nl_c)::value;
+    const char *pa, *pb;
+    frag_bases(p, pa, pb);
+    static_for<NR>([&](auto i_c) {
+      constexpr int i = decltype(i_c)::value;
+      static_for<NL>([&](auto l_c) {
+        constexpr int l = decltype(l_c)::value;
+        if constexpr (l * NR / NL == i) load(l);
+      });
+      read_one(i_c, pa, pb);
+    });
     wait_lgkmcnt0();
   };
   // the MFMAs of one K-tile; kFirst starts every chain from zero (accumulate = (k != 0))
@@ -304,15 +357,24 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmArgs args) {
     int p = 0;       // ring position of K-tile g
     auto step = [&](auto first_c) SPT_INLINE {
       // phase 2g: memory. Load ahead, store the previous output tile, read K-tile g.
-      if (valid(nx)) {
-        const int q = pos_step(p, 1);
-        if constexpr (!SPLIT) issue_a(nx, a_at(q));
-        issue_b(nx, b_at(q));
+      if constexpr (decltype(first_c)::value || !SPLIT) {
+        if (valid(nx)) {
+          const int q = pos_step(p, 1);
+          if constexpr (!SPLIT) issue_a(nx, a_at(q));
+          issue_b(nx, b_at(q));
+        }
+        if constexpr (decltype(first_c)::value) {
+          if (prev.t < args.num_tiles) epilogue(prev);
+        }
+        read_frags(p);
+      } else {
+        if (valid(nx)) {
+          const OpLoads o = prep_b(nx, b_at(pos_step(p, 1)));
+          read_frags_with_loads(p, std::integral_constant<int, LB>{}, [&](int j) SPT_INLINE { load_b(o, j); });
+        } else {
+          read_frags(p);
+        }
       }
-      if constexpr (decltype(first_c)::value) {
-        if (prev.t < args.num_tiles) epilogue(prev);
-      }
-      read_frags(p);
       barrier_sync();
       // phase 2g+1: compute K-tile g, then make sure this group's loads for K-tile g+1 (and the
       // stores issued after them) are done
@@ -346,7 +408,7 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmArgs args) {
       // stores go out here too; the wait then comes before them, so that the count of loads
       // issued after A(g+1) stays exact.
       bool loaded = false;
-      if constexpr (SPLIT) {
+      if constexpr (SPLIT && kFirst) {
         if (valid(n2)) {
           issue_a(n2, a_at(pos_step(p, 2)));
           loaded = true;
@@ -362,9 +424,19 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmArgs args) {
       if constexpr (kFirst) {
         wait_a();
         if (prev.t < args.num_tiles) epilogue(prev);
+        read_frags(p);
+      } else if constexpr (SPLIT) {
+        if (valid(n2)) {
+          const OpLoads o = prep_a(n2, a_at(pos_step(p, 2)));
+          read_frags_with_loads(p, std::integral_constant<int, LA>{}, [&](int j) SPT_INLINE { load_a(o, j); });
+          loaded = true;
+        } else {
+          read_frags(p);
+        }
+        wait_a();
+      } else {
+        read_frags(p);
       }
-      read_frags(p);
-      if constexpr (!kFirst) wait_a();
       barrier_sync();
       // phase 2g+2: compute
       compute(first_c);
