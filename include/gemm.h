@@ -219,6 +219,32 @@ gemm_status_t gemm_probe_lds_read(int swizzle, int64_t iters, void* stream);
 gemm_status_t gemm_probe_fill(const void* src, int64_t bytes, int64_t region, int64_t iters, void* stream,
                               double* bytes_moved);
 
+/*
+ * Launch a global->LDS issue-rate kernel: one workgroup of 16 waves per CU, of which the first
+ * `waves` (1..16) issue direct 1 KiB loads (buffer_load_dwordx4 ... lds) from the CU's own 64 KiB
+ * of src (so the reads hit L2), each wave keeping `depth` (1, 2, 4, 8 or 16) loads in flight;
+ * iters x 8 loads per issuing wave. Measures how fast one wave, and one CU, can stage operand tiles.
+ * *bytes_moved receives the bytes the launch loads into LDS.
+ * Errors: GEMM_ERR_INVALID (null pointer, iters < 1, waves outside 1..16, depth not a listed value,
+ * bytes below 64 KiB per CU or above 2^31 - 64 KiB), GEMM_ERR_HIP.
+ */
+gemm_status_t gemm_probe_dma_rate(const void* src, int64_t bytes, int waves, int depth, int64_t iters, void* stream,
+                                  double* bytes_moved);
+
+/*
+ * Launch a store-pattern kernel: one workgroup of 8 waves per CU; the workgroups w with
+ * w / 8 < active_per_xcd (that many per XCD) each write a 256-row x 512-byte block of dst at
+ * w*256*ldc, iters times, with 16-byte stores. Every store instruction covers rows_per_instr
+ * (2, 4, 8 or 16) rows of 1024/rows_per_instr bytes; layout 0 gives lane l row l mod
+ * rows_per_instr (the order in which an MFMA hands out rows), layout 1 puts consecutive lanes
+ * along a row. Measures how the row shape of an epilogue's stores sets its speed.
+ * *bytes_written receives the bytes the launch writes. dst must hold CU count x 256 x ldc bytes.
+ * Errors: GEMM_ERR_INVALID (null pointer, a value outside the lists, iters < 1, active_per_xcd < 1,
+ * ldc < 512 or not a multiple of 16, 256*ldc above 2^31 - 64 KiB, bytes too small), GEMM_ERR_HIP.
+ */
+gemm_status_t gemm_probe_store(void* dst, int64_t bytes, int64_t ldc, int rows_per_instr, int layout,
+                               int active_per_xcd, int64_t iters, void* stream, double* bytes_written);
+
 #ifdef __cplusplus
 }
 #endif

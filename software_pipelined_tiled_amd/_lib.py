@@ -20,7 +20,7 @@ GEMM_LOAD_AUTO, GEMM_LOAD_DMA, GEMM_LOAD_REG, GEMM_LOAD_STAGED = 0, 1, 2, 3
 EXPORTS = ("gemm_plan_create", "gemm_run", "gemm_plan_destroy", "gemm_plan_describe", "gemm_plan_workspace_bytes",
            "gemm_status_string",
            "gemm_select_config", "gemm_schedule_tile", "gemm_lds_chunk_offset", "gemm_probe_mfma_peak",
-           "gemm_probe_copy", "gemm_probe_lds_read", "gemm_probe_fill")
+           "gemm_probe_copy", "gemm_probe_lds_read", "gemm_probe_fill", "gemm_probe_dma_rate", "gemm_probe_store")
 
 
 class GemmLibraryMissing(ImportError):
@@ -87,6 +87,10 @@ def lib() -> ctypes.CDLL:
     L.gemm_probe_lds_read.argtypes = [i32, i64, vp]
     L.gemm_probe_fill.restype = i32
     L.gemm_probe_fill.argtypes = [vp, i64, i64, i64, vp, P(ctypes.c_double)]
+    L.gemm_probe_dma_rate.restype = i32
+    L.gemm_probe_dma_rate.argtypes = [vp, i64, i32, i32, i64, vp, P(ctypes.c_double)]
+    L.gemm_probe_store.restype = i32
+    L.gemm_probe_store.argtypes = [vp, i64, i64, i32, i32, i32, i64, vp, P(ctypes.c_double)]
     _lib = L
     return L
 
@@ -180,3 +184,18 @@ def gemm_probe_fill(src_ptr: int, nbytes: int, region: int, iters: int, stream: 
     _check(lib().gemm_probe_fill(src_ptr, nbytes, region, iters, stream or None, ctypes.byref(moved)),
            "gemm_probe_fill")
     return moved.value
+
+
+def gemm_probe_dma_rate(src_ptr: int, nbytes: int, waves: int, depth: int, iters: int, stream: int = 0) -> float:
+    moved = ctypes.c_double()
+    _check(lib().gemm_probe_dma_rate(src_ptr, nbytes, waves, depth, iters, stream or None, ctypes.byref(moved)),
+           "gemm_probe_dma_rate")
+    return moved.value
+
+
+def gemm_probe_store(dst_ptr: int, nbytes: int, ldc: int, rows_per_instr: int, layout: int, active_per_xcd: int,
+                     iters: int, stream: int = 0) -> float:
+    written = ctypes.c_double()
+    _check(lib().gemm_probe_store(dst_ptr, nbytes, ldc, rows_per_instr, layout, active_per_xcd, iters,
+                                  stream or None, ctypes.byref(written)), "gemm_probe_store")
+    return written.value

@@ -86,8 +86,9 @@ SPT_HD int b_row_perm32(int rho) {
 // 16x16x32 MFMA hands lane l column l mod 16 of a 16x16 block, rows 4(l/16) .. 4(l/16)+3. Within
 // each 128-row group, LDS row 16f + c holds global row 8c + f, so column c of B fragment f is
 // output column 8c + f: a lane holds columns 8c .. 8c+7 of four rows across the eight fragments of
-// its wave tile, and the 16 lanes of a quarter-wave hold one 256-byte row segment, which the
-// store path writes several times faster than the 16 rows x 64 bytes of the other layouts.
+// its wave tile, and the 16 lanes of a quarter-wave hold one 256-byte row segment. The store path
+// writes that about four times faster per CU than a quarter-wave spread over 16 rows, 16 bytes
+// each, which is what the other layouts give.
 SPT_HD int b_row_perm128(int rho) {
   const int base = rho & ~127, f = (rho >> 4) & 7, c = rho & 15;
   return base + 8 * c + f;

@@ -40,10 +40,15 @@
 // (A) phases to land, and the CU's fill path is busy in every phase.
 //
 // Inside a memory phase the eight loads are spread between the 24 fragment reads (one load, then
-// three reads). A wave issues direct global->LDS loads at about one 1 KiB instruction per 80
-// cycles however many are in flight, so eight loads occupy some 640 cycles of the phase; issued
-// as one burst they held the reads behind them and the memory phase outlasted the 64 MFMAs of
-// the other group. Interleaved, the LDS serves the reads while the loads issue.
+// three reads). A CU stages about 150 bytes of L2-resident data per ns through direct
+// global->LDS loads; with the four waves of a group issuing, each gets a 1 KiB load through
+// about every 28 ns, so eight loads hold a wave for some 350 cycles. Issued as one burst they
+// held the reads behind them and the memory phase outlasted the 64 MFMAs of the other group.
+// Interleaved, the LDS serves the reads while the loads issue.
+//
+// Epilogue: with the A fragment as the MFMA's first operand and B staged in the b_row_perm128
+// order, a lane holds 8 consecutive output columns of 4 rows, and each store instruction writes
+// four rows of 256 bytes (a quarter-wave per row).
 #include "spt_device.h"
 #include "spt_kernels.h"
 

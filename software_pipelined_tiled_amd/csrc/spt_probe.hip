@@ -88,6 +88,57 @@ __global__ void __launch_bounds__(256) fill_kernel(const char* src, unsigned nby
   __builtin_amdgcn_s_waitcnt(0);
 }
 
+// Global->LDS issue-rate probe: one workgroup of 16 waves per CU, of which the first `waves` issue
+// direct 1 KiB loads from the CU's own 64 KiB of src (L2-resident), each keeping D loads in flight
+// (a wait for vmcnt <= D-1 after every load). iters x 8 loads per issuing wave.
+template <int D>
+__global__ void __launch_bounds__(1024, 1) dma_rate_kernel(const char* src, unsigned nbytes, int waves, int64_t iters) {
+  __shared__ __attribute__((aligned(1024))) char lds[64 * 1024];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (w >= waves) return;
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(src), (short)0, (int)nbytes, 0x00020000);
+  const unsigned base = blockIdx.x * 65536u;
+  for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const unsigned chunk = (unsigned)(((it * 8 + j) * 16 + w) & 63);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(lds + ((w * 8 + j) & 63) * 1024), 16,
+                                               base + chunk * 1024u + 16u * lane, 0, 0, 0);
+      if constexpr (D == 1) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+      if constexpr (D == 2) __builtin_amdgcn_s_waitcnt(0x0F71);   // vmcnt(1)
+      if constexpr (D == 4) __builtin_amdgcn_s_waitcnt(0x0F73);   // vmcnt(3)
+      if constexpr (D == 8) __builtin_amdgcn_s_waitcnt(0x0F77);   // vmcnt(7)
+      if constexpr (D == 16) __builtin_amdgcn_s_waitcnt(0x0F7F);  // vmcnt(15)
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+}
+
+// Store-pattern probe: one workgroup of 8 waves per CU; workgroup w writes a 256-row x 512-byte
+// block at w*256*ldc, iters times, if w/8 < active (so `active` workgroups per XCD write). Every
+// store instruction writes R rows x (1024/R) bytes of 16-byte pieces: lane l takes row l mod R,
+// piece l / R (layout 0, the order an MFMA hands out rows), or row l / P, piece l mod P with
+// P = 64/R pieces per row (layout 1: consecutive lanes along a row).
+__global__ void __launch_bounds__(512, 1) store_pattern_kernel(char* dst, int64_t ldc, int R, int layout, int active,
+                                                               int64_t iters) {
+  if ((int)(blockIdx.x / 8) >= active) return;
+  const int lane = threadIdx.x & 63, v = threadIdx.x >> 6;
+  const int P = 64 / R, S = 1024 / R;  // pieces per row and bytes per row of one instruction
+  const int r = layout == 0 ? lane % R : lane / P, pc = layout == 0 ? lane / R : lane % P;
+  const __amdgpu_buffer_rsrc_t rc =
+      __builtin_amdgcn_make_buffer_rsrc(dst + (size_t)blockIdx.x * 256 * ldc, (short)0, (int)(256 * ldc), 0x00020000);
+  const u32x4 val = {(unsigned)lane, (unsigned)v, 7u, 9u};
+  const int segs = 512 / S;  // row segments of one instruction across a 512-byte row
+  for (int64_t it = 0; it < iters; ++it) {
+    for (int q = 0; q < 16; ++q) {
+      const int row = 32 * v + R * (q / segs) + r, col = S * (q % segs) + 16 * pc;
+      __builtin_amdgcn_raw_buffer_store_b128(val, rc, (unsigned)(row * ldc + col), 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+  }
+}
+
 float* g_sink[64] = {};
 
 }  // namespace
@@ -146,5 +197,46 @@ extern "C" gemm_status_t gemm_probe_fill(const void* src, int64_t bytes, int64_t
                      (unsigned)region, shared, iters);
   if (hipGetLastError() != hipSuccess) return GEMM_ERR_HIP;
   *bytes_moved = (double)cu * (double)iters * 65536.0;
+  return GEMM_OK;
+}
+
+extern "C" gemm_status_t gemm_probe_dma_rate(const void* src, int64_t bytes, int waves, int depth, int64_t iters,
+                                             void* stream, double* bytes_moved) {
+  int dev = 0, cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return GEMM_ERR_HIP;
+  if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return GEMM_ERR_HIP;
+  if (!src || !bytes_moved || iters < 1 || waves < 1 || waves > 16 || bytes > 0x7FFF0000LL ||
+      bytes < (int64_t)cu * 65536)
+    return GEMM_ERR_INVALID;
+  const dim3 g((unsigned)cu), b(1024);
+  const hipStream_t st = (hipStream_t)stream;
+  const unsigned n = (unsigned)bytes;
+  switch (depth) {
+    case 1: hipLaunchKernelGGL(dma_rate_kernel<1>, g, b, 0, st, (const char*)src, n, waves, iters); break;
+    case 2: hipLaunchKernelGGL(dma_rate_kernel<2>, g, b, 0, st, (const char*)src, n, waves, iters); break;
+    case 4: hipLaunchKernelGGL(dma_rate_kernel<4>, g, b, 0, st, (const char*)src, n, waves, iters); break;
+    case 8: hipLaunchKernelGGL(dma_rate_kernel<8>, g, b, 0, st, (const char*)src, n, waves, iters); break;
+    case 16: hipLaunchKernelGGL(dma_rate_kernel<16>, g, b, 0, st, (const char*)src, n, waves, iters); break;
+    default: return GEMM_ERR_INVALID;
+  }
+  if (hipGetLastError() != hipSuccess) return GEMM_ERR_HIP;
+  *bytes_moved = (double)cu * (double)waves * (double)iters * 8.0 * 1024.0;
+  return GEMM_OK;
+}
+
+extern "C" gemm_status_t gemm_probe_store(void* dst, int64_t bytes, int64_t ldc, int rows_per_instr, int layout,
+                                          int active_per_xcd, int64_t iters, void* stream, double* bytes_written) {
+  int dev = 0, cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return GEMM_ERR_HIP;
+  if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return GEMM_ERR_HIP;
+  const bool r_ok = rows_per_instr == 2 || rows_per_instr == 4 || rows_per_instr == 8 || rows_per_instr == 16;
+  if (!dst || !bytes_written || !r_ok || (layout != 0 && layout != 1) || iters < 1 || active_per_xcd < 1 ||
+      ldc < 512 || ldc % 16 != 0 || 256 * ldc > 0x7FFF0000LL || bytes < (int64_t)cu * 256 * ldc)
+    return GEMM_ERR_INVALID;
+  hipLaunchKernelGGL(store_pattern_kernel, dim3((unsigned)cu), dim3(512), 0, (hipStream_t)stream, (char*)dst, ldc,
+                     rows_per_instr, layout, active_per_xcd, iters);
+  if (hipGetLastError() != hipSuccess) return GEMM_ERR_HIP;
+  const int wgs = active_per_xcd * 8 < cu ? active_per_xcd * 8 : cu;
+  *bytes_written = (double)wgs * (double)iters * 131072.0;
   return GEMM_OK;
 }

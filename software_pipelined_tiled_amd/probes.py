@@ -5,6 +5,10 @@
     lds     the LDS read-pattern kernels, one launch per swizzle (read the counters with rocprofv3)
     fill    global->LDS fill rate per CU: each workgroup re-reading its own 64 KiB (L2-resident),
             and streaming 4 MiB of its own (L2 misses)
+    dma     global->LDS issue rate: 1, 4, 8 or 16 issuing waves per CU, each keeping 1..16 loads in
+            flight, L2-resident reads
+    store   epilogue store shapes: rows per store instruction (16, 8, 4, 2) x lane layout, with 1, 8
+            or 32 writing workgroups per XCD
 """
 from __future__ import annotations
 
@@ -54,6 +58,38 @@ def fill(iters: int = 2000) -> dict:
     return res
 
 
+def dma(iters: int = 1000) -> list[dict]:
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    nbytes = cus * 65536
+    src = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    rows = []
+    for waves in (1, 4, 8, 16):
+        for depth in (1, 2, 4, 8, 16):
+            _lib.gemm_probe_dma_rate(src.data_ptr(), nbytes, waves, depth, 4)
+            ms, moved = _timed(lambda: _lib.gemm_probe_dma_rate(src.data_ptr(), nbytes, waves, depth, iters))
+            per_cu = moved / (ms * 1e6) / cus
+            rows.append({"waves": waves, "depth": depth, "B_per_ns_per_cu": per_cu,
+                         "B_per_ns_per_wave": per_cu / waves, "ns_per_load_per_wave": 1024.0 / (per_cu / waves)})
+    return rows
+
+
+def store(iters: int = 20, ldc: int = 32768) -> list[dict]:
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    nbytes = cus * 256 * ldc
+    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    rows = []
+    for r, layout in ((16, 0), (16, 1), (8, 1), (4, 1), (2, 1)):
+        for active in (1, 8, 32):
+            _lib.gemm_probe_store(dst.data_ptr(), nbytes, ldc, r, layout, active, 2)
+            ms, written = _timed(lambda: _lib.gemm_probe_store(dst.data_ptr(), nbytes, ldc, r, layout, active, iters))
+            wgs = min(active * 8, cus)
+            rows.append({"rows_per_instr": r, "layout": "mfma rows" if layout == 0 else "along a row",
+                         "active_per_xcd": active, "us_per_128KiB": ms * 1e3 / iters,
+                         "GB_per_s_per_cu": written / wgs / (ms * 1e-3) / 1e9,
+                         "GB_per_s_total": written / (ms * 1e-3) / 1e9})
+    return rows
+
+
 def lds(iters: int = 2000) -> None:
     for sw in (-1, 0, 1, 2, 3, 4):
         _lib.gemm_probe_lds_read(sw, iters)
@@ -68,6 +104,12 @@ if __name__ == "__main__":
         print(f"{copy():.1f} GB/s")
     elif what == "fill":
         print(fill())
+    elif what == "dma":
+        for row in dma():
+            print(row)
+    elif what == "store":
+        for row in store():
+            print(row)
     elif what == "lds":
         lds()
         print("lds probes launched: swizzles -1, 0, 1, 2, 3, 4 in this order")
