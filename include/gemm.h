@@ -207,6 +207,14 @@ gemm_status_t gemm_probe_copy(const void* src, void* dst, int64_t bytes, void* s
 gemm_status_t gemm_probe_lds_read(int swizzle, int64_t iters, void* stream);
 
 /*
+ * Launch an LDS read-bandwidth kernel: one workgroup of 8 waves per CU, each wave keeping 16
+ * independent ds_read_b128 (16 bytes per lane, consecutive addresses, conflict-free) in flight,
+ * `iters` times. *bytes_read receives the bytes the launch reads from LDS.
+ * Errors: GEMM_ERR_INVALID (iters < 1, null bytes_read), GEMM_ERR_HIP.
+ */
+gemm_status_t gemm_probe_lds_bw(int64_t iters, void* stream, double* bytes_read);
+
+/*
  * Launch a global->LDS fill kernel (the staging path of the GEMM's mainloop): one workgroup of
  * 4 waves per CU; per iteration every wave issues 16 direct 1 KiB loads (buffer_load_dwordx4 ...
  * lds), two iterations in flight. Workgroup w reads the `region` bytes of src at w*region,

@@ -20,7 +20,7 @@ GEMM_LOAD_AUTO, GEMM_LOAD_DMA, GEMM_LOAD_REG, GEMM_LOAD_STAGED = 0, 1, 2, 3
 EXPORTS = ("gemm_plan_create", "gemm_run", "gemm_plan_destroy", "gemm_plan_describe", "gemm_plan_workspace_bytes",
            "gemm_status_string",
            "gemm_select_config", "gemm_schedule_tile", "gemm_lds_chunk_offset", "gemm_probe_mfma_peak",
-           "gemm_probe_copy", "gemm_probe_lds_read", "gemm_probe_fill", "gemm_probe_dma_rate", "gemm_probe_store")
+           "gemm_probe_copy", "gemm_probe_lds_read", "gemm_probe_lds_bw", "gemm_probe_fill", "gemm_probe_dma_rate", "gemm_probe_store")
 
 
 class GemmLibraryMissing(ImportError):
@@ -85,6 +85,8 @@ def lib() -> ctypes.CDLL:
     L.gemm_probe_copy.argtypes = [vp, vp, i64, vp]
     L.gemm_probe_lds_read.restype = i32
     L.gemm_probe_lds_read.argtypes = [i32, i64, vp]
+    L.gemm_probe_lds_bw.restype = i32
+    L.gemm_probe_lds_bw.argtypes = [i64, vp, P(ctypes.c_double)]
     L.gemm_probe_fill.restype = i32
     L.gemm_probe_fill.argtypes = [vp, i64, i64, i64, vp, P(ctypes.c_double)]
     L.gemm_probe_dma_rate.restype = i32
@@ -199,3 +201,9 @@ def gemm_probe_store(dst_ptr: int, nbytes: int, ldc: int, rows_per_instr: int, l
     _check(lib().gemm_probe_store(dst_ptr, nbytes, ldc, rows_per_instr, layout, active_per_xcd, iters,
                                   stream or None, ctypes.byref(written)), "gemm_probe_store")
     return written.value
+
+
+def gemm_probe_lds_bw(iters: int, stream: int = 0) -> float:
+    nbytes = ctypes.c_double()
+    _check(lib().gemm_probe_lds_bw(iters, stream or None, ctypes.byref(nbytes)), "gemm_probe_lds_bw")
+    return nbytes.value

@@ -139,6 +139,26 @@ __global__ void __launch_bounds__(512, 1) store_pattern_kernel(char* dst, int64_
   }
 }
 
+// LDS read-bandwidth probe: one workgroup of 8 waves per CU; every wave keeps 16 independent
+// ds_read_b128 (conflict-free, 16 bytes per lane at consecutive addresses) in flight, then waits.
+__global__ void __launch_bounds__(512, 1) lds_bw_kernel(unsigned* sink, int64_t iters) {
+  __shared__ __attribute__((aligned(1024))) char smem[128 * 1024];
+  for (int i = threadIdx.x; i < 128 * 1024 / 4; i += 512) ((unsigned*)smem)[i] = (unsigned)i;
+  __syncthreads();
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const unsigned base = (unsigned)(uintptr_t)(const lds_void_t*)smem + (unsigned)(w * 1024 + 16 * lane);
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (int64_t it = 0; it < iters; ++it) {
+    u32x4 v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v[j]) : "v"(base), "i"(j * 8192 % 57344));
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc ^= v[j];
+  }
+  if ((acc[0] ^ acc[1] ^ acc[2] ^ acc[3]) == 0x12345678u) sink[0] = 1u;  // keeps the reads alive
+}
+
 float* g_sink[64] = {};
 
 }  // namespace
@@ -238,5 +258,17 @@ extern "C" gemm_status_t gemm_probe_store(void* dst, int64_t bytes, int64_t ldc,
   if (hipGetLastError() != hipSuccess) return GEMM_ERR_HIP;
   const int wgs = active_per_xcd * 8 < cu ? active_per_xcd * 8 : cu;
   *bytes_written = (double)wgs * (double)iters * 131072.0;
+  return GEMM_OK;
+}
+
+extern "C" gemm_status_t gemm_probe_lds_bw(int64_t iters, void* stream, double* bytes_read) {
+  if (iters < 1 || !bytes_read) return GEMM_ERR_INVALID;
+  int dev = 0, cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return GEMM_ERR_HIP;
+  if (!g_sink[dev] && hipMalloc(&g_sink[dev], sizeof(float)) != hipSuccess) return GEMM_ERR_HIP;
+  if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return GEMM_ERR_HIP;
+  hipLaunchKernelGGL(lds_bw_kernel, dim3(cu), dim3(512), 0, (hipStream_t)stream, (unsigned*)g_sink[dev], iters);
+  if (hipGetLastError() != hipSuccess) return GEMM_ERR_HIP;
+  *bytes_read = (double)cu * 512.0 * (double)iters * 16.0 * 16.0;
   return GEMM_OK;
 }

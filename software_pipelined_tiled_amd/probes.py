@@ -7,6 +7,7 @@
             and streaming 4 MiB of its own (L2 misses)
     dma     global->LDS issue rate: 1, 4, 8 or 16 issuing waves per CU, each keeping 1..16 loads in
             flight, L2-resident reads
+    ldsbw   LDS read bandwidth per CU: 8 waves per CU, 16 independent ds_read_b128 per wave in flight
     store   epilogue store shapes: rows per store instruction (16, 8, 4, 2) x lane layout, with 1, 8
             or 32 writing workgroups per XCD
 """
@@ -90,6 +91,15 @@ def store(iters: int = 20, ldc: int = 32768) -> list[dict]:
     return rows
 
 
+def ldsbw(iters: int = 4000) -> dict:
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    _lib.gemm_probe_lds_bw(10)
+    ms, nbytes = _timed(lambda: _lib.gemm_probe_lds_bw(iters))
+    per_cu = nbytes / (ms * 1e6) / cus
+    return {"B_per_ns_per_cu": per_cu, "B_per_clk_per_cu_if_2.4GHz": per_cu / 2.4,
+            "TB_per_s_total": nbytes / (ms * 1e-3) / 1e12}
+
+
 def lds(iters: int = 2000) -> None:
     for sw in (-1, 0, 1, 2, 3, 4):
         _lib.gemm_probe_lds_read(sw, iters)
@@ -110,6 +120,8 @@ if __name__ == "__main__":
     elif what == "store":
         for row in store():
             print(row)
+    elif what == "ldsbw":
+        print(ldsbw())
     elif what == "lds":
         lds()
         print("lds probes launched: swizzles -1, 0, 1, 2, 3, 4 in this order")

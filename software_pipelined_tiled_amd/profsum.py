@@ -43,11 +43,17 @@ def _code_tokens(text: str) -> str:
     return " ".join(text.split())
 
 
+# the measurement probes are built into the same library but share no code with the GEMM path
+_NOT_GEMM = ("spt_probe.hip",)
+
+
 def kernel_source_hash() -> str:
-    """Hash of the kernel sources' code (comments and layout ignored); a traffic figure is only
+    """Hash of the GEMM path's sources (comments and layout ignored); a traffic figure is only
     valid for the code it was taken on."""
     h = hashlib.sha256()
     for p in sorted(glob.glob(os.path.join(HERE, "csrc", "*"))):
+        if os.path.basename(p) in _NOT_GEMM:
+            continue
         with open(p, encoding="utf-8") as f:
             h.update(os.path.basename(p).encode())
             h.update(_code_tokens(f.read()).encode())
