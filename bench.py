@@ -96,7 +96,7 @@ def main() -> int:
 
     import software_pipelined_tiled_amd as spt
     import synthetic_inputs as si
-    from software_pipelined_tiled_amd.profsum import kernel_label, kernel_source_hash
+    from software_pipelined_tiled_amd.profsum import kernel_source_hash, run_kernel_label
 
     torch.cuda.set_device(0)
     M, N, K, a_bits, b_bits, in_dt, out_dt = si.workload_operands(args.workload, args.shape_index)
@@ -111,6 +111,7 @@ def main() -> int:
     config = json.loads(args.config) if args.config else None
     plan = spt.Plan(M, N, K, tdt[in_dt], tdt[out_dt], config=config)
     desc = plan.describe()
+    parts = plan.parts()
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
 
@@ -138,7 +139,8 @@ def main() -> int:
     flop = 2.0 * M * N * K
     value = flop / (ms_per_step * 1e-3) / 1e12
     achieved = flop / (avg_launch_ms * 1e-3) / 1e12
-    kernel_name = kernel_label(desc, DTYPE_NAME[in_dt], DTYPE_NAME[out_dt])
+    run_config = {"plan": desc, "parts": parts}
+    kernel_name = run_kernel_label(run_config, DTYPE_NAME[in_dt], DTYPE_NAME[out_dt])
     traffic = load_traffic(args.workload, args.shape_index, kernel_name)
     compulsory = (M * K + N * K) * 2 + M * N * (4 if out_dt == 2 else 2)
     hbm_bound = compulsory / (PEAK_HBM_GBS * 1e9) > flop / (PEAK_TFLOPS * 1e12)
@@ -189,6 +191,7 @@ def main() -> int:
         "config": {"workload": args.workload, "M": M, "N": N, "K": K, "in_dtype": DTYPE_NAME[in_dt],
                    "out_dtype": DTYPE_NAME[out_dt], "accumulate": "f32",
                    "distribution": si.WORKLOADS[args.workload]["dist"], "kernel": kernel_name, "plan": desc,
+                   **({"parts": parts} if parts["dim"] >= 0 else {}),
                    "b_cache": "cold (rotated copies)" if args.cold else "warm"},
         "roofline": ({"bound": "hbm", "achieved": compulsory / (avg_launch_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
                       "unit": "GB/s", "frac": compulsory / (avg_launch_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,

@@ -137,8 +137,23 @@ gemm_status_t gemm_plan_destroy(gemm_plan_t plan);
 /* Bytes of device workspace the plan owns (0 when none). Errors: GEMM_ERR_INVALID on NULL. */
 gemm_status_t gemm_plan_workspace_bytes(gemm_plan_t plan, int64_t* out);
 
-/* Copy the configuration `plan` launches into *out. Errors: GEMM_ERR_INVALID on NULL. */
+/* Copy the configuration `plan` launches into *out (for a plan in two parts, part 0's, with this
+ * plan's load path). Errors: GEMM_ERR_INVALID on NULL. */
 gemm_status_t gemm_plan_describe(gemm_plan_t plan, gemm_config_t* out);
+
+/*
+ * How a plan covers the output. Without an override, a plan may cut the problem in two when one
+ * tile size would leave the last round of workgroups mostly idle (wave quantisation): part 0 takes
+ * whole rounds of its tiles, part 1 is planned on its own by the same model (smaller tiles, or K
+ * split), and gemm_run launches them one after the other on the same stream, over the same
+ * operands (after the staging copy, when the plan stages).
+ *   *dim     -1: one part; 1: the output's columns are cut at *at (part 0: columns [0, at),
+ *            part 1: [at, N)); 0: its rows are cut at *at
+ *   first    part 0's configuration (the plan's own when *dim is -1); may be NULL
+ *   second   part 1's configuration (untouched when *dim is -1); may be NULL
+ * Errors: GEMM_ERR_INVALID (null plan, dim or at).
+ */
+gemm_status_t gemm_plan_parts(gemm_plan_t plan, int* dim, int64_t* at, gemm_config_t* first, gemm_config_t* second);
 
 /* Static, human-readable name of a status code ("GEMM_OK", ...). Never NULL. */
 const char* gemm_status_string(gemm_status_t status);
@@ -157,6 +172,16 @@ gemm_status_t gemm_select_config(int64_t M, int64_t N, int64_t K, gemm_dtype_t a
                                  gemm_dtype_t b_dtype, gemm_dtype_t c_dtype, int64_t lda,
                                  int64_t ldb, int64_t ldc, int cu_count, int lds_bytes,
                                  gemm_config_t* out);
+
+/*
+ * The cut gemm_plan_create would make without an override (see gemm_plan_parts), on a device with
+ * `cu_count` compute units and `lds_bytes` of LDS per workgroup: *dim -1 (and *first the single
+ * configuration), or the cut and both parts' configurations. Same argument checks and errors as
+ * gemm_select_config; dim and at must not be NULL.
+ */
+gemm_status_t gemm_select_parts(int64_t M, int64_t N, int64_t K, gemm_dtype_t a_dtype, gemm_dtype_t b_dtype,
+                                gemm_dtype_t c_dtype, int64_t lda, int64_t ldb, int64_t ldc, int cu_count,
+                                int lds_bytes, int* dim, int64_t* at, gemm_config_t* first, gemm_config_t* second);
 
 /*
  * Work unit handled by workgroup `wg` (0 <= wg < grid) on its `round`-th pass of the persistent

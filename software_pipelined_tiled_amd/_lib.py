@@ -18,8 +18,8 @@ GEMM_LOAD_AUTO, GEMM_LOAD_DMA, GEMM_LOAD_REG, GEMM_LOAD_STAGED = 0, 1, 2, 3
 
 # every entry point include/gemm.h declares
 EXPORTS = ("gemm_plan_create", "gemm_run", "gemm_plan_destroy", "gemm_plan_describe", "gemm_plan_workspace_bytes",
-           "gemm_status_string",
-           "gemm_select_config", "gemm_schedule_tile", "gemm_lds_chunk_offset", "gemm_probe_mfma_peak",
+           "gemm_plan_parts", "gemm_status_string",
+           "gemm_select_config", "gemm_select_parts", "gemm_schedule_tile", "gemm_lds_chunk_offset", "gemm_probe_mfma_peak",
            "gemm_probe_copy", "gemm_probe_lds_read", "gemm_probe_lds_bw", "gemm_probe_fill", "gemm_probe_dma_rate", "gemm_probe_store")
 
 
@@ -71,6 +71,11 @@ def lib() -> ctypes.CDLL:
     L.gemm_plan_describe.argtypes = [vp, P(GemmConfig)]
     L.gemm_plan_workspace_bytes.restype = i32
     L.gemm_plan_workspace_bytes.argtypes = [vp, P(i64)]
+    L.gemm_plan_parts.restype = i32
+    L.gemm_plan_parts.argtypes = [vp, P(i32), P(i64), P(GemmConfig), P(GemmConfig)]
+    L.gemm_select_parts.restype = i32
+    L.gemm_select_parts.argtypes = [i64, i64, i64, i32, i32, i32, i64, i64, i64, i32, i32, P(i32), P(i64),
+                                    P(GemmConfig), P(GemmConfig)]
     L.gemm_status_string.restype = ctypes.c_char_p
     L.gemm_status_string.argtypes = [i32]
     L.gemm_select_config.restype = i32
@@ -130,6 +135,29 @@ def gemm_plan_describe(plan: int) -> dict:
     c = GemmConfig()
     _check(lib().gemm_plan_describe(plan, ctypes.byref(c)), "gemm_plan_describe")
     return c.as_dict()
+
+
+def _parts_dict(dim, at, first, second) -> dict:
+    d = {"dim": dim.value, "at": at.value, "first": first.as_dict()}
+    if dim.value >= 0:
+        d["second"] = second.as_dict()
+    return d
+
+
+def gemm_plan_parts(plan: int) -> dict:
+    """{'dim': -1 | 0 (rows cut) | 1 (columns cut), 'at': cut position, 'first': config[, 'second': config]}"""
+    dim, at, first, second = ctypes.c_int(), ctypes.c_int64(), GemmConfig(), GemmConfig()
+    _check(lib().gemm_plan_parts(plan, ctypes.byref(dim), ctypes.byref(at), ctypes.byref(first),
+                                 ctypes.byref(second)), "gemm_plan_parts")
+    return _parts_dict(dim, at, first, second)
+
+
+def gemm_select_parts(M, N, K, a_dtype, b_dtype, c_dtype, lda, ldb, ldc, cu_count=256, lds_bytes=160 * 1024) -> dict:
+    dim, at, first, second = ctypes.c_int(), ctypes.c_int64(), GemmConfig(), GemmConfig()
+    _check(lib().gemm_select_parts(M, N, K, a_dtype, b_dtype, c_dtype, lda, ldb, ldc, cu_count, lds_bytes,
+                                   ctypes.byref(dim), ctypes.byref(at), ctypes.byref(first), ctypes.byref(second)),
+           "gemm_select_parts")
+    return _parts_dict(dim, at, first, second)
 
 
 def gemm_plan_workspace_bytes(plan: int) -> int:

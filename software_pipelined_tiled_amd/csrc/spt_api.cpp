@@ -28,6 +28,12 @@ struct gemm_plan_s {
   int64_t ldw;             // row length of a partial plane (elements)
   const void* fn_reduce;
   const void* fn_stage;
+  // A plan cut in two (wave quantisation): part[0] covers output columns (split_dim 1) or rows
+  // (split_dim 0) [0, split_at), part[1] the rest; each is a plan of its own over the operands this
+  // plan's kernels read (its staged copies when it stages). split_dim -1: one part, this plan.
+  int split_dim;
+  int64_t split_at;
+  gemm_plan_s* part[2];
 };
 
 namespace {
@@ -186,6 +192,75 @@ gemm_config_t choose(int64_t M, int64_t N, int64_t K, const Candidate* menu, int
   return best;
 }
 
+// Relative MFMA rate of a menu configuration (0.2 for one not on the menus).
+double rate_of(const gemm_config_t& c) {
+  const bool reg = c.load_path == GEMM_LOAD_REG;
+  const Candidate* menu = reg ? kRegMenu : kDmaMenu;
+  const int n = reg ? 2 : 4;
+  for (int i = 0; i < n; ++i)
+    if (menu[i].bm == c.bm && menu[i].bn == c.bn && menu[i].bk == c.bk && menu[i].stages == c.stages &&
+        menu[i].waves == c.waves)
+      return menu[i].rate;
+  return 0.2;
+}
+
+// The single configuration `choose` picks and its modelled time.
+double best_single(int64_t M, int64_t N, int64_t K, int path, int cu_count, int lds_bytes, gemm_config_t* out) {
+  *out = choose(M, N, K, kDmaMenu, 4, path, cu_count, lds_bytes);
+  return model_time(*out, rate_of(*out), M, N, K, cu_count, lds_bytes);
+}
+
+// Wave quantisation: with T tiles on G workgroup slots, a last round of T mod G tiles runs at a
+// fraction of the device. Cutting the output in two, a first part of whole rounds of one tile size
+// and the rest planned on its own (the same menu and model: smaller tiles, or K split), can cost
+// less than the rounds of the single choice. Each menu tile and each cut along N or M that gives
+// the first part k whole rounds is modelled; a cut is taken when it is modelled at least 10 %
+// faster than the single choice, counting one more kernel launch.
+struct Parts {
+  int dim;     // 1: columns cut at `at`; 0: rows
+  int64_t at;
+  gemm_config_t first, second;
+};
+constexpr double kLaunchSeconds = 5e-6;
+bool choose_parts(int64_t M, int64_t N, int64_t K, int cu_count, int lds_bytes, Parts* out) {
+  if (M <= 0 || N <= 0 || K <= 0) return false;
+  gemm_config_t single;
+  const double t_single = best_single(M, N, K, GEMM_LOAD_DMA, cu_count, lds_bytes, &single);
+  double best = 0.9 * t_single;
+  bool have = false;
+  for (const Candidate& c : kDmaMenu) {
+    gemm_config_t cfg{};
+    cfg.bm = c.bm; cfg.bn = c.bn; cfg.bk = c.bk; cfg.stages = c.stages; cfg.waves = c.waves; cfg.mfma = 16;
+    cfg.persistent = 1; cfg.group_m = 8; cfg.load_path = GEMM_LOAD_DMA; cfg.splits = 1;
+    cfg.lds_bytes = ring_bytes(cfg);
+    const int64_t tm = ceil_div(M, c.bm), tn = ceil_div(N, c.bn), T = tm * tn;
+    const int64_t G = (int64_t)cu_count * groups_per_cu(cfg, lds_bytes);
+    if (T <= G || T % G == 0) continue;
+    for (int dim = 1; dim >= 0; --dim) {
+      for (int64_t k = 1; k <= T / G; ++k) {
+        const int64_t lines = dim == 1 ? (k * G) / tm : (k * G) / tn;  // tile columns (rows) of part 0
+        if (lines < 1 || lines >= (dim == 1 ? tn : tm)) continue;
+        const int64_t at = lines * (dim == 1 ? c.bn : c.bm);
+        const int64_t M0 = dim == 1 ? M : at, N0 = dim == 1 ? at : N;
+        const int64_t M1 = dim == 1 ? M : M - at, N1 = dim == 1 ? N - at : N;
+        const double t0 = model_time(cfg, c.rate, M0, N0, K, cu_count, lds_bytes);
+        gemm_config_t second;
+        const double t1 = best_single(M1, N1, K, GEMM_LOAD_DMA, cu_count, lds_bytes, &second);
+        const double t = t0 + t1 + kLaunchSeconds;
+        if (t < best) {
+          best = t;
+          have = true;
+          out->dim = dim;
+          out->at = at;
+          out->first = cfg;
+          out->second = second;
+        }
+      }
+    }
+  }
+  return have;
+}
+
 void finish_config(gemm_config_t& c, int64_t M, int64_t N, int cu_count, int lds_bytes, int& tm, int& tn) {
   tm = (int)ceil_div(M, c.bm);
   tn = (int)ceil_div(N, c.bn);
@@ -310,8 +385,31 @@ gemm_status_t gemm_plan_create(gemm_plan_t* out, int64_t M, int64_t N, int64_t K
   p->M = M; p->N = N; p->K = K; p->lda = lda; p->ldb = ldb; p->ldc = ldc;
   p->in_dtype = a_dtype; p->out_dtype = c_dtype;
   p->dev = dev;
+  p->split_dim = -1;
   st = select_impl(M, N, K, a_dtype, b_dtype, c_dtype, lda, ldb, ldc, cu, lds, config, &p->cfg, &p->cfg_reg);
   if (st != GEMM_OK) { delete p; return st; }
+  // the built-in choice may cut the output in two (wave quantisation); each part is a plan over
+  // the operands the kernels read: the staged copies (rows of K rounded up to 8) or A and B
+  const bool staged_path = p->cfg.load_path == GEMM_LOAD_STAGED;
+  Parts parts;
+  if (!config && is_dma(p->cfg.load_path) &&
+      choose_parts(M, N, staged_path ? round_up(K, 8) : K, cu, lds, &parts)) {
+    const int64_t kk = staged_path ? round_up(K, 8) : K;
+    const int64_t la = staged_path ? kk : lda, lb = staged_path ? kk : ldb;
+    const int64_t M0 = parts.dim == 1 ? M : parts.at, N0 = parts.dim == 1 ? parts.at : N;
+    const int64_t M1 = parts.dim == 1 ? M : M - parts.at, N1 = parts.dim == 1 ? N - parts.at : N;
+    st = gemm_plan_create(&p->part[0], M0, N0, kk, a_dtype, b_dtype, c_dtype, la, lb, ldc, &parts.first);
+    if (st == GEMM_OK)
+      st = gemm_plan_create(&p->part[1], M1, N1, kk, a_dtype, b_dtype, c_dtype, la, lb, ldc, &parts.second);
+    if (st != GEMM_OK) {
+      (void)gemm_plan_destroy(p->part[0]);
+      delete p;
+      return st;
+    }
+    p->split_dim = parts.dim;
+    p->split_at = parts.at;
+    p->cfg.splits = 1;  // this plan only stages (when it does); the parts run the mainloops
+  }
   const bool split = p->cfg.splits > 1;
   p->fn_main = kernel_fn(p->cfg, a_dtype, split ? GEMM_F32 : c_dtype);
   p->fn_reg = kernel_fn(p->cfg_reg, a_dtype, c_dtype);
@@ -322,7 +420,7 @@ gemm_status_t gemm_plan_create(gemm_plan_t* out, int64_t M, int64_t N, int64_t K
   p->tiles_m_reg = (int)ceil_div(M, p->cfg_reg.bm);
   p->tiles_n_reg = (int)ceil_div(N, p->cfg_reg.bn);
   if (!p->fn_main) { delete p; return GEMM_ERR_UNSUPPORTED; }
-  const WsLayout w = ws_layout(M, N, K, p->cfg.load_path, p->cfg.splits);
+  const WsLayout w = ws_layout(M, N, K, p->cfg.load_path, p->split_dim >= 0 ? 1 : p->cfg.splits);
   p->kp = w.kp;
   p->ldw = w.ldw;
   p->stage_a_off = w.stage_a;
@@ -332,6 +430,8 @@ gemm_status_t gemm_plan_create(gemm_plan_t* out, int64_t M, int64_t N, int64_t K
     void* ws = nullptr;
     if (hipMalloc(&ws, (size_t)w.total) != hipSuccess) {
       (void)hipGetLastError();
+      (void)gemm_plan_destroy(p->part[0]);
+      (void)gemm_plan_destroy(p->part[1]);
       delete p;
       return GEMM_ERR_NOMEM;
     }
@@ -344,6 +444,10 @@ gemm_status_t gemm_plan_create(gemm_plan_t* out, int64_t M, int64_t N, int64_t K
 gemm_status_t gemm_plan_destroy(gemm_plan_t plan) {
   if (!plan) return GEMM_OK;
   gemm_status_t st = GEMM_OK;
+  for (gemm_plan_s* part : plan->part) {
+    const gemm_status_t sp = gemm_plan_destroy(part);
+    if (sp != GEMM_OK) st = sp;
+  }
   if (plan->ws) {
     int cur = 0;
     const bool switched = hipGetDevice(&cur) == hipSuccess && cur != plan->dev && hipSetDevice(plan->dev) == hipSuccess;
@@ -360,12 +464,57 @@ gemm_status_t gemm_plan_destroy(gemm_plan_t plan) {
 gemm_status_t gemm_plan_describe(gemm_plan_t plan, gemm_config_t* out) {
   if (!plan || !out) return GEMM_ERR_INVALID;
   *out = plan->cfg;
+  if (plan->part[0]) {  // part 0's mainloop, on this plan's load path
+    *out = plan->part[0]->cfg;
+    out->load_path = plan->cfg.load_path;
+  }
+  return GEMM_OK;
+}
+
+gemm_status_t gemm_plan_parts(gemm_plan_t plan, int* dim, int64_t* at, gemm_config_t* first, gemm_config_t* second) {
+  if (!plan || !dim || !at) return GEMM_ERR_INVALID;
+  *dim = plan->split_dim;
+  *at = plan->split_dim >= 0 ? plan->split_at : 0;
+  if (first) *first = plan->part[0] ? plan->part[0]->cfg : plan->cfg;
+  if (second && plan->part[1]) *second = plan->part[1]->cfg;
+  return GEMM_OK;
+}
+
+gemm_status_t gemm_select_parts(int64_t M, int64_t N, int64_t K, gemm_dtype_t a_dtype, gemm_dtype_t b_dtype,
+                                gemm_dtype_t c_dtype, int64_t lda, int64_t ldb, int64_t ldc, int cu_count,
+                                int lds_bytes, int* dim, int64_t* at, gemm_config_t* first, gemm_config_t* second) {
+  if (!dim || !at) return GEMM_ERR_INVALID;
+  gemm_config_t single;
+  const gemm_status_t st =
+      select_impl(M, N, K, a_dtype, b_dtype, c_dtype, lda, ldb, ldc, cu_count, lds_bytes, nullptr, &single, nullptr);
+  if (st != GEMM_OK) return st;
+  *dim = -1;
+  *at = 0;
+  if (first) *first = single;
+  Parts parts;
+  const bool staged = single.load_path == GEMM_LOAD_STAGED;
+  if (!is_dma(single.load_path) || !choose_parts(M, N, staged ? round_up(K, 8) : K, cu_count, lds_bytes, &parts))
+    return GEMM_OK;
+  *dim = parts.dim;
+  *at = parts.at;
+  gemm_config_t c0 = parts.first, c1 = parts.second;
+  int tm, tn;
+  finish_config(c0, parts.dim == 1 ? M : parts.at, parts.dim == 1 ? parts.at : N, cu_count, lds_bytes, tm, tn);
+  finish_config(c1, parts.dim == 1 ? M : M - parts.at, parts.dim == 1 ? N - parts.at : N, cu_count, lds_bytes, tm,
+                tn);
+  if (first) *first = c0;
+  if (second) *second = c1;
   return GEMM_OK;
 }
 
 gemm_status_t gemm_plan_workspace_bytes(gemm_plan_t plan, int64_t* out) {
   if (!plan || !out) return GEMM_ERR_INVALID;
-  *out = plan->ws ? ws_layout(plan->M, plan->N, plan->K, plan->cfg.load_path, plan->cfg.splits).total : 0;
+  *out = plan->ws ? ws_layout(plan->M, plan->N, plan->K, plan->cfg.load_path, plan->split_dim >= 0 ? 1 : plan->cfg.splits).total
+                 : 0;
+  for (gemm_plan_s* part : plan->part) {
+    int64_t b = 0;
+    if (part && gemm_plan_workspace_bytes(part, &b) == GEMM_OK) *out += b;
+  }
   return GEMM_OK;
 }
 
@@ -409,7 +558,19 @@ gemm_status_t gemm_run(gemm_plan_t plan, const void* A, const void* B, void* C, 
       B = g.dB;
       K = lda = ldb = plan->kp;
     }
-  } else if (cfg->load_path == GEMM_LOAD_DMA && !aligned) {
+  }
+  if (plan->split_dim >= 0) {
+    // the two parts, over the same (possibly staged) operands: part 1 starts `split_at` columns
+    // (rows) into B and C (A and C)
+    st = gemm_run(plan->part[0], A, B, C, stream);
+    if (st != GEMM_OK) return st;
+    const int64_t es = plan->out_dtype == GEMM_F32 ? 4 : 2, at = plan->split_at;
+    const char* A1 = (const char*)A + (plan->split_dim == 0 ? at * lda * 2 : 0);
+    const char* B1 = (const char*)B + (plan->split_dim == 1 ? at * ldb * 2 : 0);
+    char* C1 = (char*)C + (plan->split_dim == 1 ? at * es : at * plan->ldc * es);
+    return gemm_run(plan->part[1], A1, B1, C1, stream);
+  }
+  if (cfg->load_path == GEMM_LOAD_DMA && !aligned) {
     if (!plan->fn_reg) return GEMM_ERR_UNSUPPORTED;
     cfg = &plan->cfg_reg;
     fn = plan->fn_reg;

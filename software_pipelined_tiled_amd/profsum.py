@@ -79,6 +79,19 @@ def kernel_matches(plan: dict, name: str) -> bool:
     return mangled in name
 
 
+def plan_parts(config: dict) -> list[dict]:
+    """The configurations whose mainloop kernels one gemm_run launches: the plan's, or both parts'
+    of a plan cut in two (bench.py records the cut under config["parts"])."""
+    parts = config.get("parts")
+    if parts and parts.get("dim", -1) >= 0:
+        return [parts["first"], parts["second"]]
+    return [config["plan"]]
+
+
+def run_kernel_label(config: dict, in_dt: str, out_dt: str) -> str:
+    return " + ".join(kernel_label(p, in_dt, out_dt) for p in plan_parts(config))
+
+
 def kernel_label(plan: dict, in_dt: str, out_dt: str) -> str:
     """Short name of the mainloop kernel a plan launches, with its configuration (a split-K plan's
     mainloop writes fp32 partial planes)."""
@@ -115,21 +128,24 @@ def kernel_stats(stats_csv: str, bench_json: str, out_md: str, command: str) -> 
            f"Plan: {json.dumps(plan)}", "",
            "| kernel | calls | average (us) | min (us) | max (us) | share of GPU time |",
            "|---|---|---|---|---|---|"]
+    plans = plan_parts(line["config"])
+    runs = line["steps"] + line["warmup"]
     gemm_avg = None
-    aux = {}  # the other kernels of one gemm_run: split-K reduction, operand staging copy
+    terms = []  # (label, average us, dispatches per run) of the kernels of one gemm_run
     for r in rows:
         name = r.get("Name", r.get("KernelName", "?"))
         avg = float(r["AverageNs"]) / 1e3
         out.append(f"| `{name[:110]}` | {r['Calls']} | {avg:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
                    f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
-        if kernel_matches(plan, name):
-            gemm_avg = avg
-        for k in ("splitk_reduce_kernel", "stage_kernel"):
-            if k in name:
-                aux[k] = avg
+        if _run_kernel(plans, name):
+            per = max(1, round(int(r["Calls"]) / runs))
+            label = next((k for k in AUX_KERNELS if k in name), "mainloop")
+            terms.append((label, avg, per))
+            if label == "mainloop":
+                gemm_avg = avg
     ev_us = line["extra"]["avg_launch_ms"] * 1e3
-    run_avg = (gemm_avg or 0.0) + sum(aux.values())
-    parts = " + ".join([f"mainloop {gemm_avg:.1f}"] + [f"{k} {v:.1f}" for k, v in aux.items()]) if gemm_avg else ""
+    run_avg = sum(avg * per for _, avg, per in terms)
+    parts = " + ".join(f"{lab} {avg:.1f}" + (f" x {per}" if per > 1 else "") for lab, avg, per in terms)
     ro = line["roofline"]
     out += ["", f"gemm_run time from HIP events in the same run: {ev_us:.1f} us (rocprofv3 average "
                 f"{parts} = {run_avg:.1f} us, ratio {ev_us / run_avg:.3f})." if gemm_avg else
@@ -141,28 +157,51 @@ def kernel_stats(stats_csv: str, bench_json: str, out_md: str, command: str) -> 
     print("\n".join(out))
 
 
-def _counter_means(path: str, counter: str, plan: dict) -> tuple[float, float, int]:
-    """Mean per-dispatch value (bytes) of `counter` for the GEMM (skipping its first, cold launch)
-    and for the copy kernel."""
+AUX_KERNELS = ("splitk_reduce_kernel", "stage_kernel")  # the other kernels of one gemm_run
+
+
+def _run_kernel(plans: list[dict], name: str) -> bool:
+    return any(kernel_matches(p, name) for p in plans) or any(k in name for k in AUX_KERNELS)
+
+
+def _counter_means(path: str, counter: str, plans: list[dict], per_run: int) -> tuple[float, float, int]:
+    """Mean value (bytes) of `counter` per gemm_run, summed over the `per_run` dispatches of one
+    run (mainloops, reduction, staging copy), skipping the first, cold run; and the copy kernel's."""
     gemm, copy = [], []
     for r in _rows(path):
         if r["Counter_Name"] != counter:
             continue
         v = float(r["Counter_Value"]) * 1024.0  # rocprofv3 reports these two counters in KiB
-        if kernel_matches(plan, r["Kernel_Name"]):
+        if _run_kernel(plans, r["Kernel_Name"]):
             gemm.append(v)
         elif "copy16_kernel" in r["Kernel_Name"]:
             copy.append(v)
-    if len(gemm) < 2 or not copy:
-        raise SystemExit(f"{path}: need >= 2 GEMM and >= 1 copy dispatches with {counter}")
-    return statistics.mean(gemm[1:]), statistics.mean(copy), len(gemm) - 1
+    runs = len(gemm) // per_run
+    if runs < 2 or not copy:
+        raise SystemExit(f"{path}: need >= 2 runs of {per_run} GEMM dispatches and >= 1 copy dispatch with {counter}")
+    rest = gemm[per_run:runs * per_run]
+    return sum(rest) / (runs - 1), statistics.mean(copy), runs - 1
+
+
+def _dispatches_per_run(csv_path: str, plans: list[dict], runs: int) -> int:
+    """Dispatches of one gemm_run, from the kernel trace or counter file of `runs` runs."""
+    n = 0
+    for r in _rows(csv_path):
+        name = r.get("Kernel_Name", r.get("Name", ""))
+        if "Counter_Name" in r and r["Counter_Name"] not in ("FETCH_SIZE", "WRITE_SIZE"):
+            continue
+        if _run_kernel(plans, name):
+            n += 1
+    return max(1, round(n / max(runs, 1)))
 
 
 def traffic(fetch_csv: str, write_csv: str, bench_json: str, out_json: str, command: str) -> None:
     line = _bench_line(bench_json)
-    plan = line["config"]["plan"]
-    f_gemm, f_copy, nf = _counter_means(fetch_csv, "FETCH_SIZE", plan)
-    w_gemm, w_copy, nw = _counter_means(write_csv, "WRITE_SIZE", plan)
+    plans = plan_parts(line["config"])
+    runs = line["steps"] + line["warmup"]
+    per_run = _dispatches_per_run(fetch_csv, plans, runs)
+    f_gemm, f_copy, nf = _counter_means(fetch_csv, "FETCH_SIZE", plans, per_run)
+    w_gemm, w_copy, nw = _counter_means(write_csv, "WRITE_SIZE", plans, per_run)
     f_scale, w_scale = COPY_BYTES / f_copy, COPY_BYTES / w_copy
     c = line["config"]
     out_bytes = 4 if c["out_dtype"] == "f32" else 2

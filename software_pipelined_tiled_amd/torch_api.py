@@ -34,6 +34,9 @@ class Plan:
     def describe(self) -> dict:
         return _lib.gemm_plan_describe(self.handle)
 
+    def parts(self) -> dict:
+        return _lib.gemm_plan_parts(self.handle)
+
     def workspace_bytes(self) -> int:
         return _lib.gemm_plan_workspace_bytes(self.handle)
 

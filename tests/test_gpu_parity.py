@@ -286,6 +286,29 @@ def test_staged_operands_bit_exact(M, N, K, lda, ldb):
             check_full(a, b, K, in_dt, si.BF16, c, N, exact=True)
 
 
+@pytest.mark.parametrize("K,lda", [(1024, 1024), (1023, 1023)])
+def test_two_part_plan_bit_exact(K, lda):
+    # 4096 x 5119 at 256x256 is 16 x 20 = 320 tiles for 256 workgroups: the plan runs columns
+    # [0, 4096) as one full round of 256x256 tiles and the other 1023 as a plan of its own (K = 1023
+    # with rows of 1023: both parts read the staged copies). Every column of a set of rows, on both
+    # sides of the cut and at tile edges, is compared bit for bit.
+    M, N = 4096, 5119
+    a = ints(M, K, si.F16, 501 + K, ld=lda)
+    b = ints(N, K, si.F16, 502 + K, ld=lda)
+    plan = spt.Plan(M, N, K, torch.float16, torch.float32, lda, lda, N)
+    parts = plan.parts()
+    plan.close()
+    assert parts["dim"] == 1 and parts["at"] == 4096 and parts["first"]["bm"] == 256
+    c, desc = run_gpu(a, b, K, si.F16, si.F32)
+    if K % 8:
+        assert desc["load_path"] == spt.GEMM_LOAD_STAGED
+    rng = np.random.default_rng(K)
+    rows = sorted(set(rng.integers(0, M, 40).tolist()) | {0, 127, 128, 255, 256, 4095})
+    c_ref, _, _ = orc.gemm(np.ascontiguousarray(a[rows]), b, K, si.F16, si.F32)
+    got = np.ascontiguousarray(c[rows, :N])
+    assert np.array_equal(got.view(np.uint32), c_ref.view(np.uint32))
+
+
 def test_workspace_sizes():
     p = spt.Plan(300, 500, 4096, torch.float16, torch.float16, config=cfg(64, 64, 4, splits=4))
     assert p.workspace_bytes() == 4 * 300 * 504 * 4

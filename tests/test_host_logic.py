@@ -116,6 +116,39 @@ def test_config_choice(name):
         assert c["bm"] == 64  # M = 32: a larger tile would be mostly padding
 
 
+def test_two_part_choice():
+    # 4093 x 5119 (K staged to 3072): 320 tiles of 256x256 for 256 workgroups, a second round a
+    # quarter full. The plan cuts the columns at 4096 (16 x 16 tiles: one full round of the
+    # two-wave-group kernel) and plans the last 1023 columns on their own.
+    p = spt.gemm_select_parts(4093, 5119, 3071, F16, F16, F16, 3071, 3071, 5119)
+    assert p["dim"] == 1 and p["at"] == 4096
+    f, s = p["first"], p["second"]
+    assert (f["bm"], f["bn"], f["waves"]) == (256, 256, 8) and math.ceil(4093 / 256) * (4096 // 256) == 256
+    assert s["bm"] * s["bn"] < 256 * 256  # the rest runs on smaller tiles
+    # shapes that fill whole rounds, or have fewer tiles than workgroups, stay in one part
+    for M, N, K in ((8192, 8192, 8192), (4096, 4096, 4096), (16384, 16384, 1024), (32, 8192, 8192),
+                    (8192, 1024, 28672), (256, 256, 256)):
+        assert spt.gemm_select_parts(M, N, K, BF16, BF16, BF16, K, K, N)["dim"] == -1
+
+
+@pytest.mark.parametrize("M,N,K", [(4093, 5119, 3072), (5000, 3000, 2048), (3000, 7000, 4096), (4096, 5119, 1024),
+                                   (6000, 2100, 8192), (300, 90000, 512)])
+def test_two_part_cut_covers_the_output(M, N, K):
+    p = spt.gemm_select_parts(M, N, K, F16, F16, F16, K, K, N)
+    if p["dim"] < 0:
+        return
+    f, s, at = p["first"], p["second"], p["at"]
+    full = N if p["dim"] == 1 else M
+    assert 0 < at < full
+    # part 0 ends on a tile edge and runs whole rounds of its tiles (at most one tile line short)
+    assert at % (f["bn"] if p["dim"] == 1 else f["bm"]) == 0
+    t0 = (math.ceil(M / f["bm"]) * (at // f["bn"]) if p["dim"] == 1 else (at // f["bm"]) * math.ceil(N / f["bn"]))
+    g0 = 256 * (1 if f["bm"] * f["bn"] >= 128 * 128 else 2)
+    line = math.ceil(M / f["bm"]) if p["dim"] == 1 else math.ceil(N / f["bn"])
+    assert t0 % g0 == 0 or g0 - t0 % g0 < line
+    assert s["grid"] >= 1 and f["grid"] >= 1
+
+
 def test_split_choice_small_k_and_limits():
     # K too short to split (fewer than 16 K-tiles): one range per tile
     c = spt.gemm_select_config(64, 64, 512, F16, F16, F16, 512, 512, 64, 256, 160 * 1024)
