@@ -10,6 +10,10 @@
     ldsbw   LDS read bandwidth per CU: 8 waves per CU, 16 independent ds_read_b128 per wave in flight
     store   epilogue store shapes: rows per store instruction (16, 8, 4, 2) x lane layout, with 1, 8
             or 32 writing workgroups per XCD
+    library 8192^3 bf16 (N(0,1)/sqrt(K) inputs drawn with torch) through this library's default plan,
+            its 4-wave 256x256 split-ring plan, and, for context only, torch.mm (the vendor GEMM
+            library), in alternating blocks of launches; prints TFLOP/s per block. Run it under
+            rocprofv3 --pmc to compare clock, MFMA utilisation and instruction mix per kernel.
 """
 from __future__ import annotations
 
@@ -100,6 +104,31 @@ def ldsbw(iters: int = 4000) -> dict:
             "TB_per_s_total": nbytes / (ms * 1e-3) / 1e12}
 
 
+def library(reps: int = 3, launches: int = 6) -> list[dict]:
+    from .torch_api import Plan
+
+    M = N = K = 8192
+    g = torch.Generator(device="cuda").manual_seed(0)
+    A = (torch.randn(M, K, device="cuda", generator=g) / K ** 0.5).to(torch.bfloat16)
+    B = (torch.randn(N, K, device="cuda", generator=g) / K ** 0.5).to(torch.bfloat16)
+    C = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    four_wave = dict(bm=256, bn=256, bk=64, stages=5, waves=4, mfma=16, persistent=1, group_m=8, load_path=1,
+                     grid=0, lds_bytes=0, splits=1)
+    plans = {"default plan": Plan(M, N, K, torch.bfloat16, torch.bfloat16),
+             "4-wave split ring": Plan(M, N, K, torch.bfloat16, torch.bfloat16, config=four_wave)}
+    sp = torch.cuda.current_stream().cuda_stream
+    runs = {name: (lambda p=p: p.run_ptrs(A.data_ptr(), B.data_ptr(), C.data_ptr(), sp)) for name, p in plans.items()}
+    runs["torch.mm (context)"] = lambda: torch.mm(A, B.t(), out=C)
+    rows = []
+    for r in range(reps):
+        for name, fn in runs.items():
+            ms, _ = _timed(lambda: [fn() for _ in range(launches)])
+            rows.append({"rep": r, "kernel": name, "TFLOP/s": 2.0 * M * N * K * launches / (ms * 1e-3) / 1e12})
+    for p in plans.values():
+        p.close()
+    return rows
+
+
 def lds(iters: int = 2000) -> None:
     for sw in (-1, 0, 1, 2, 3, 4):
         _lib.gemm_probe_lds_read(sw, iters)
@@ -122,6 +151,9 @@ if __name__ == "__main__":
             print(row)
     elif what == "ldsbw":
         print(ldsbw())
+    elif what == "library":
+        for row in library():
+            print(row, flush=True)
     elif what == "lds":
         lds()
         print("lds probes launched: swizzles -1, 0, 1, 2, 3, 4 in this order")

@@ -286,6 +286,62 @@ def lds(counter_csv: str, out_md: str, command: str) -> None:
     print("\n".join(out))
 
 
+LIBRARY_KERNELS = (("gemm_pp_kernel", "two-group (default plan)"), ("gemm_dma_kernel", "4-wave split ring"),
+                   ("Cijk", "vendor library via torch.mm (context)"))
+COMPARE_COUNTERS = ("SQ_INSTS_LDS", "SQ_INSTS_SALU", "SQ_INSTS_VALU", "SQ_INSTS_VMEM_RD", "SQ_INSTS_VMEM_WR",
+                    "SQ_WAVES", "SQ_WAIT_ANY", "SQ_WAVE_CYCLES", "SQ_VMEM_TA_ADDR_FIFO_FULL",
+                    "SQ_LDS_BANK_CONFLICT", "FETCH_SIZE")
+
+
+def compare(counter_csvs: list[str], agent_csv: str, out_md: str, command: str, flop: float) -> None:
+    """Per-kernel means of the `library` probe's counter passes: clock, MFMA utilisation, instruction mix."""
+    gpu = next(r for r in _rows(agent_csv) if r.get("Agent_Type") == "GPU")
+    n_se, n_cu = int(gpu["Num_Shader_Banks"]), int(gpu["Cu_Count"])
+    per = {}  # label -> list of per-dispatch dicts (dispatches of one pass keep their own clock)
+    for path in counter_csvs:
+        disp = {}
+        for r in _rows(path):
+            label = next((lab for key, lab in LIBRARY_KERNELS if key in r["Kernel_Name"]), None)
+            if label is None:
+                continue
+            d = disp.setdefault((label, int(r["Dispatch_Id"])),
+                                {"dur": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9})
+            d[r["Counter_Name"]] = float(r["Counter_Value"])
+        firsts = set()
+        for (label, did), d in sorted(disp.items(), key=lambda x: x[0][1]):
+            if label not in firsts:  # the first launch of each kernel in a pass warms caches and clocks
+                firsts.add(label)
+                continue
+            per.setdefault(label, []).append(d)
+    out = ["# Clock, MFMA utilisation and instruction mix on 8192^3 bf16: this library against the vendor library",
+           "", f"Command: `{command}`", "",
+           "The vendor library's GEMM (hipBLASLt, reached through torch.mm) is run for context only: it is neither",
+           "the oracle nor part of this library. Means over the launches of each kernel after its first in each",
+           f"pass. clock = SQ_BUSY_CYCLES / {n_se} shader engines / duration; MFMA utilisation = 2MNK / duration /",
+           f"({n_cu} CUs x 4096 flop/clk x clock). Instruction counts are per launch, summed over the chip.", "",
+           "| kernel | launches | duration (us) | TFLOP/s | clock (GHz) | MFMA util. at that clock | "
+           + " | ".join(COMPARE_COUNTERS) + " |",
+           "|---|---|---|---|---|---|" + "---|" * len(COMPARE_COUNTERS)]
+    for _, label in LIBRARY_KERNELS:
+        ds = per.get(label, [])
+        if not ds:
+            continue
+        clk = [d["SQ_BUSY_CYCLES"] / n_se / d["dur"] for d in ds if "SQ_BUSY_CYCLES" in d]
+        util = [flop / d["dur"] / (n_cu * 4096 * (d["SQ_BUSY_CYCLES"] / n_se / d["dur"])) for d in ds
+                if "SQ_BUSY_CYCLES" in d]
+        dur = statistics.mean(d["dur"] for d in ds)
+        cells = []
+        for c in COMPARE_COUNTERS:
+            v = [d[c] for d in ds if c in d]
+            cells.append(f"{statistics.mean(v):.4g}" if v else "")
+        out.append(f"| {label} | {len(ds)} | {dur * 1e6:.1f} | {flop / dur / 1e12:.1f} | "
+                   f"{statistics.mean(clk) / 1e9 if clk else float('nan'):.3f} | "
+                   f"{statistics.mean(util) if util else float('nan'):.3f} | " + " | ".join(cells) + " |")
+    with open(out_md, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print("\n".join(out))
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="what", required=True)
@@ -301,8 +357,13 @@ def main(argv=None) -> int:
     d = sub.add_parser("lds")
     d.add_argument("counter_csv"), d.add_argument("out_md")
     d.add_argument("--command", required=True)
+    cp = sub.add_parser("compare")
+    cp.add_argument("agent_csv"), cp.add_argument("out_md"), cp.add_argument("counter_csvs", nargs="+")
+    cp.add_argument("--command", required=True)
     a = ap.parse_args(argv)
-    if a.what == "lds":
+    if a.what == "compare":
+        compare(a.counter_csvs, a.agent_csv, a.out_md, a.command, 2.0 * 8192 ** 3)
+    elif a.what == "lds":
         lds(a.counter_csv, a.out_md, a.command)
     elif a.what == "clock":
         clock(a.counter_csv, a.agent_csv, a.bench_json, a.out_md, a.command)
