@@ -145,17 +145,32 @@ int pick_splits(const gemm_config_t& c, int64_t M, int64_t N, int64_t K, int cu_
 }
 
 // The tile menu, with each kernel's sustained MFMA rate per CU relative to the two-wave-group
-// 256x256 kernel (measured on large square problems: about 1450, 1160, 1020 and 500 TFLOP/s).
+// 256x256 kernel (measured on large square problems: about 1450, 1160, 1020 and 500 TFLOP/s). The
+// 64x64 tile with 128-deep K-tiles keeps twice the bytes of the 64-deep one in flight: it is there
+// for the skinny shapes, whose time is the operand stream rather than the MFMAs. Its rate is set
+// above the streaming bounds below (on 32 x 8192 x 8192 it measured 0.52 of the 256x256 kernel's
+// per-CU rate while streaming B at 5.8 TB/s), so that the model takes those bounds for it.
 struct Candidate { int bm, bn, bk, stages, waves; double rate; };
 const Candidate kDmaMenu[] = {{256, 256, 64, 5, 8, 1.0}, {256, 128, 64, 3, 4, 0.8}, {128, 128, 64, 4, 4, 0.7},
-                              {64, 64, 64, 4, 4, 0.35}};
+                              {64, 64, 64, 4, 4, 0.35}, {64, 64, 128, 4, 4, 0.6}};
 const Candidate kRegMenu[] = {{128, 128, 64, 2, 4, 0.35}, {64, 64, 64, 2, 4, 0.2}};
+constexpr int kDmaMenuSize = (int)(sizeof(kDmaMenu) / sizeof(kDmaMenu[0]));
+constexpr int kRegMenuSize = (int)(sizeof(kRegMenu) / sizeof(kRegMenu[0]));
 
-// Modelled time of a configuration (seconds): the rounds of work units every workgroup slot runs,
-// each unit its MFMA work at the kernel's rate plus about one K-tile of fill and store, and, for a
-// split K, the fp32 partial planes written and read back by the reduction.
+// Modelled time of a configuration (seconds), the largest of three bounds, plus the reduction:
+//   * MFMA: the rounds of work units every workgroup slot runs, each unit its MFMA work at the
+//     kernel's rate plus about one K-tile of fill and store;
+//   * ring: each unit streams (bm + bn) rows of its K range through a ring that holds S-1 of its S
+//     K-tiles in flight, and a load takes about kLoadLatency to land, so a workgroup moves at most
+//     (S-1)/S of its ring bytes per kLoadLatency;
+//   * HBM: A, B and C once each at the sustained streaming rate;
+// and, for a split K, the fp32 partial planes written and read back by the reduction. The ring and
+// HBM bounds decide only the skinny shapes (few flops per operand byte); on the others the MFMA
+// bound is several times larger.
 constexpr double kCuFlops = 1450e12 / 256;  // two-wave-group kernel, per CU
 constexpr double kHbmBytes = 4.5e12;        // streaming rate of the reduction
+constexpr double kHbmStream = 6.0e12;       // operand streaming rate of a whole launch
+constexpr double kLoadLatency = 1.0e-6;     // fitted: a 64x64 tile streams about 48 KiB/us per 64 KiB of ring
 double model_time(const gemm_config_t& c, double rate, int64_t M, int64_t N, int64_t K, int cu_count,
                   int lds_bytes) {
   const int gpc = groups_per_cu(c, lds_bytes);
@@ -163,8 +178,15 @@ double model_time(const gemm_config_t& c, double rate, int64_t M, int64_t N, int
   const int64_t rounds = ceil_div(units, (int64_t)cu_count * gpc);
   const int64_t kt_per = ceil_div(ceil_div(K, c.bk), c.splits);
   const double unit = 2.0 * c.bm * c.bn * (double)(kt_per + 1) * c.bk / (rate * kCuFlops / gpc);
+  const double unit_bytes = 2.0 * (c.bm + c.bn) * (double)kt_per * c.bk;
+  const double in_flight = (double)ring_bytes(c) * (c.stages > 1 ? c.stages - 1 : 1) / c.stages;
+  const double ring = rounds * unit_bytes * kLoadLatency / in_flight;
+  const double hbm = (2.0 * (double)(M + N) * K + 4.0 * (double)M * N) / kHbmStream;
   const double reduce = c.splits > 1 ? (2.0 * partial_bytes(M, N, c.splits) + 2.0 * M * N) / kHbmBytes : 0.0;
-  return rounds * unit + reduce;
+  double t = rounds * unit;
+  if (ring > t) t = ring;
+  if (hbm > t) t = hbm;
+  return t + reduce;
 }
 
 // The candidate of least modelled time, each with K unsplit and with K split as pick_splits says. A
@@ -196,7 +218,7 @@ gemm_config_t choose(int64_t M, int64_t N, int64_t K, const Candidate* menu, int
 double rate_of(const gemm_config_t& c) {
   const bool reg = c.load_path == GEMM_LOAD_REG;
   const Candidate* menu = reg ? kRegMenu : kDmaMenu;
-  const int n = reg ? 2 : 4;
+  const int n = reg ? kRegMenuSize : kDmaMenuSize;
   for (int i = 0; i < n; ++i)
     if (menu[i].bm == c.bm && menu[i].bn == c.bn && menu[i].bk == c.bk && menu[i].stages == c.stages &&
         menu[i].waves == c.waves)
@@ -206,7 +228,7 @@ double rate_of(const gemm_config_t& c) {
 
 // The single configuration `choose` picks and its modelled time.
 double best_single(int64_t M, int64_t N, int64_t K, int path, int cu_count, int lds_bytes, gemm_config_t* out) {
-  *out = choose(M, N, K, kDmaMenu, 4, path, cu_count, lds_bytes);
+  *out = choose(M, N, K, kDmaMenu, kDmaMenuSize, path, cu_count, lds_bytes);
   return model_time(*out, rate_of(*out), M, N, K, cu_count, lds_bytes);
 }
 
@@ -310,11 +332,11 @@ gemm_status_t select_impl(int64_t M, int64_t N, int64_t K, gemm_dtype_t a, gemm_
     if (!find_entry_for_path(cfg)) return GEMM_ERR_INVALID;
     if (cfg.lds_bytes > lds_bytes) return GEMM_ERR_INVALID;
   } else if (dma_ok) {
-    cfg = choose(M, N, K, kDmaMenu, 4, GEMM_LOAD_DMA, cu_count, lds_bytes);
+    cfg = choose(M, N, K, kDmaMenu, kDmaMenuSize, GEMM_LOAD_DMA, cu_count, lds_bytes);
   } else if (stage_ok) {
-    cfg = choose(M, N, round_up(K, 8), kDmaMenu, 4, GEMM_LOAD_STAGED, cu_count, lds_bytes);
+    cfg = choose(M, N, round_up(K, 8), kDmaMenu, kDmaMenuSize, GEMM_LOAD_STAGED, cu_count, lds_bytes);
   } else {
-    cfg = choose(M, N, K, kRegMenu, 2, GEMM_LOAD_REG, cu_count, lds_bytes);
+    cfg = choose(M, N, K, kRegMenu, kRegMenuSize, GEMM_LOAD_REG, cu_count, lds_bytes);
   }
   int tm, tn;
   finish_config(cfg, M, N, cu_count, lds_bytes, tm, tn);
@@ -327,7 +349,7 @@ gemm_status_t select_impl(int64_t M, int64_t N, int64_t K, gemm_dtype_t a, gemm_
     return GEMM_ERR_UNSUPPORTED;
   *out = cfg;
   if (out_reg) {
-    gemm_config_t r = choose(M, N, K, kRegMenu, 2, GEMM_LOAD_REG, cu_count, lds_bytes);
+    gemm_config_t r = choose(M, N, K, kRegMenu, kRegMenuSize, GEMM_LOAD_REG, cu_count, lds_bytes);
     r.persistent = cfg.persistent;
     r.group_m = cfg.group_m;
     finish_config(r, M, N, cu_count, lds_bytes, tm, tn);

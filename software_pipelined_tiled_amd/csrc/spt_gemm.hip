@@ -374,6 +374,7 @@ const KernelEntry* dma_kernel_table(int* count) {
       make_entry<128, 128, 64, 2, 2, 2>(),
       make_entry<128, 128, 64, 1, 2, 2>(),
       make_entry<64, 64, 64, 4, 2, 2>(),
+      make_entry<64, 64, 128, 4, 2, 2>(),
       make_entry<64, 64, 64, 2, 2, 2>(),
   };
   *count = (int)(sizeof(table) / sizeof(table[0]));

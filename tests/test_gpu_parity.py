@@ -91,6 +91,21 @@ def test_ring_configs_k_around_depth(K, bk, s, waves):
     check_full(a, b, K, si.BF16, si.F32, c, N, exact=True)
 
 
+@pytest.mark.parametrize("K", [8, 120, 128, 136, 384, 512, 520, 5 * 128 + 24])
+@pytest.mark.parametrize("persistent", [1, 0])
+def test_deep_64_tile_bit_exact(K, persistent):
+    # the 64x64 tile with 128-deep K-tiles (two 64-wide LDS groups per K-tile, four stages): fewer
+    # K-tiles than stages, about as many, and more; K tails inside the first and the second group;
+    # M = 32 as in the skinny workload (half the tile's rows past the edge) and a ragged 3 x 2 grid
+    for M, N in ((32, 3 * 64 - 24), (2 * 64 + 37, 2 * 64 - 5)):
+        a = ints(M, K, si.F16, 40 + K + M)
+        b = ints(N, K, si.F16, 41 + K + N)
+        c, desc = run_gpu(a, b, K, si.F16, si.F32,
+                          config=cfg(64, 64, 4, bk=128, persistent=persistent, grid=2 if persistent else 0))
+        assert (desc["bm"], desc["bk"], desc["stages"]) == (64, 128, 4)
+        check_full(a, b, K, si.F16, si.F32, c, N, exact=True)
+
+
 @pytest.mark.parametrize("bm,bn,s", REG_CONFIGS)
 def test_reg_configs_bit_exact(bm, bn, s):
     M, N, K = 2 * bm + 7, bn + 9, 3 * 64 + 13  # K not a multiple of 8: element-masked tail
@@ -212,8 +227,9 @@ def test_mfma32_split_k_and_real_values():
 # ------------------------------------------------------------------------- split-K and staging
 
 # (bm, bn, bk, stages, waves) of every mainloop kernel that runs split-K units
-SPLIT_CONFIGS = [(64, 64, 64, 4, 4), (128, 128, 64, 4, 4), (256, 128, 64, 3, 4), (256, 256, 64, 2, 4),
-                 (256, 256, 64, 5, 4), (256, 256, 32, 4, 4), (256, 256, 64, 5, 8), (256, 256, 64, 2, 8)]
+SPLIT_CONFIGS = [(64, 64, 64, 4, 4), (64, 64, 128, 4, 4), (128, 128, 64, 4, 4), (256, 128, 64, 3, 4),
+                 (256, 256, 64, 2, 4), (256, 256, 64, 5, 4), (256, 256, 32, 4, 4), (256, 256, 64, 5, 8),
+                 (256, 256, 64, 2, 8)]
 
 
 @pytest.mark.parametrize("bm,bn,bk,s,waves", SPLIT_CONFIGS)
@@ -354,4 +370,6 @@ def test_workload_c1_small_full_through_each_dma_config():
         c, _ = run_gpu(a, b, k, i_dt, o_dt, config=ring_cfg(bk, s, waves))
         check_full(a, b, k, i_dt, o_dt, c, n)
     c, _ = run_gpu(a, b, k, i_dt, o_dt, config=ring_cfg(64, 5, 8, mfma=32))
+    check_full(a, b, k, i_dt, o_dt, c, n)
+    c, _ = run_gpu(a, b, k, i_dt, o_dt, config=cfg(64, 64, 4, bk=128))
     check_full(a, b, k, i_dt, o_dt, c, n)
