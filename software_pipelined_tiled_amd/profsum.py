@@ -113,6 +113,11 @@ def _bench_line(path: str) -> dict:
     return json.loads(lines[-1])
 
 
+def gemm_runs(line: dict) -> int:
+    """gemm_run calls in a bench.py process (warm-up and timed steps)."""
+    return int(line["extra"].get("gemm_runs", line["steps"] + line["warmup"]))
+
+
 def _rows(path: str) -> list[dict]:
     with open(path, newline="") as f:
         return list(csv.DictReader(f))
@@ -129,7 +134,7 @@ def kernel_stats(stats_csv: str, bench_json: str, out_md: str, command: str) -> 
            "| kernel | calls | average (us) | min (us) | max (us) | share of GPU time |",
            "|---|---|---|---|---|---|"]
     plans = plan_parts(line["config"])
-    runs = line["steps"] + line["warmup"]
+    runs = gemm_runs(line)
     gemm_avg = None
     terms = []  # (label, average us, dispatches per run) of the kernels of one gemm_run
     for r in rows:
@@ -198,7 +203,7 @@ def _dispatches_per_run(csv_path: str, plans: list[dict], runs: int) -> int:
 def traffic(fetch_csv: str, write_csv: str, bench_json: str, out_json: str, command: str) -> None:
     line = _bench_line(bench_json)
     plans = plan_parts(line["config"])
-    runs = line["steps"] + line["warmup"]
+    runs = gemm_runs(line)
     per_run = _dispatches_per_run(fetch_csv, plans, runs)
     f_gemm, f_copy, nf = _counter_means(fetch_csv, "FETCH_SIZE", plans, per_run)
     w_gemm, w_copy, nw = _counter_means(write_csv, "WRITE_SIZE", plans, per_run)
