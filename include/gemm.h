@@ -60,7 +60,8 @@ typedef enum {
   GEMM_LOAD_REG = 2,  /* global->VGPR->LDS copies with per-element K masking (any alignment) */
   GEMM_LOAD_STAGED = 3 /* copy A and B into workspace rows of roundup(K, 8) elements (zero
                           padded), then DMA; any alignment. AUTO takes it when DMA is not
-                          possible and the copies fit in 3 GiB */
+                          possible, the copies fit in 3 GiB and each source operand spans
+                          under 2 GiB (M rows of lda, N rows of ldb) */
 } gemm_load_path_t;
 
 /*
@@ -111,7 +112,8 @@ typedef struct gemm_plan_s* gemm_plan_t;
  *   config    NULL for the built-in choice, else an explicit configuration (validated)
  * Errors: GEMM_ERR_INVALID (null out, bad sizes or ld, invalid override),
  *         GEMM_ERR_UNSUPPORTED (dtype pair, a tile whose row span exceeds 2^31 bytes, an override
- *         whose workspace exceeds the caps: 1 GiB of partial planes, 3 GiB of staged operands),
+ *         whose workspace exceeds the caps: 1 GiB of partial planes, 3 GiB of staged operands,
+ *         or a staged override whose source operand spans 2 GiB or more),
  *         GEMM_ERR_HIP (no usable gfx950 device), GEMM_ERR_NOMEM (host or device allocation).
  */
 gemm_status_t gemm_plan_create(gemm_plan_t* out, int64_t M, int64_t N, int64_t K,

@@ -84,6 +84,12 @@ gemm_status_t check_args(int64_t M, int64_t N, int64_t K, gemm_dtype_t a, gemm_d
 }
 
 // Offsets inside one tile are 32-bit: a tile's rows must span less than 2^31 bytes.
+// The staging copy addresses a source operand through one buffer descriptor with 32-bit byte
+// offsets, and reads up to 20 bytes around each 16-byte chunk (from the dword holding its first byte).
+bool stage_source_fits(int64_t rows, int64_t ld, int64_t K) {
+  return rows <= 0 || 4 + ((rows - 1) * ld + K) * 2 + 20 < ((int64_t)1 << 31);
+}
+
 bool offsets_fit(const gemm_config_t& c, int64_t lda, int64_t ldb, int64_t ldc, gemm_dtype_t out) {
   const int64_t es = out == GEMM_F32 ? 4 : 2;
   const int64_t lim = (int64_t)1 << 31;
@@ -314,7 +320,8 @@ gemm_status_t select_impl(int64_t M, int64_t N, int64_t K, gemm_dtype_t a, gemm_
   if (st != GEMM_OK) return st;
   if (cu_count < 1 || lds_bytes < 1) return GEMM_ERR_INVALID;
   const bool dma_ok = dma_eligible(K, lda, ldb);
-  const bool stage_ok = stage_bytes(M, N, K) <= kMaxStageBytes;
+  const bool stage_ok = stage_bytes(M, N, K) <= kMaxStageBytes && stage_source_fits(M, lda, K) &&
+                        stage_source_fits(N, ldb, K);
   gemm_config_t cfg;
   if (ovr) {
     st = validate_override(*ovr);

@@ -10,9 +10,10 @@
 //     copy writes the operand into rows of Kp = K rounded up to a multiple of 8 elements, with the
 //     padding columns zero; the mainloop then runs over Kp, where each padding term adds 0.
 //
-// Both are plain streaming kernels: 16-byte accesses where alignment allows, one pass over the
-// data, a grid-stride loop over 8-element chunks (32-bit chunk indices: the host caps the
-// workspace so the counts fit).
+// Both are plain streaming kernels: one pass over the data, a grid-stride loop over 8-element
+// chunks (32-bit chunk indices: the host caps the workspace so the counts fit). The reduction
+// uses 16-byte accesses where alignment allows; the staging copy reads each 16-byte chunk of a
+// 2-byte-aligned row as the dword-aligned 20 bytes around it and writes it with one 16-byte store.
 #include "spt_device.h"
 #include "spt_kernels.h"
 
@@ -70,28 +71,64 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(ReduceArgs r) {
   }
 }
 
-// dst rows of ldd = Kp elements (16-byte aligned) from src rows of ld elements (any 2-byte
-// alignment): dst[row, k] = src[row, k] for k < K, 0 for K <= k < Kp. Chunk q < rows_a * cpr is
-// chunk q mod cpr of row q / cpr of A; the chunks after them are B's, the same way (cpr = Kp / 8).
-__global__ void __launch_bounds__(256) stage_kernel(StageArgs g) {
-  const unsigned cpr = (unsigned)g.ldd >> 3;
-  const unsigned na = (unsigned)g.rows_a * cpr;
-  const unsigned total = na + (unsigned)g.rows_b * cpr;
-  for (unsigned q = blockIdx.x * 256u + threadIdx.x; q < total; q += gridDim.x * 256u) {
-    const bool is_a = q < na;
-    const unsigned qq = is_a ? q : q - na;
-    const unsigned row = qq / cpr;
-    const int k = (int)(8u * (qq - row * cpr));
-    const unsigned short* s = (const unsigned short*)(is_a ? g.A : g.B) + (size_t)row * (is_a ? g.lda : g.ldb) + k;
-    unsigned short h[8];
+// 16 bytes at byte offset `off` (any 2-byte alignment) of the buffer `r`, whose first `end` bytes
+// are the operand: the dword-aligned 20 bytes that hold them, in two loads, then shifted into place a
+// dword at a time (v_alignbyte takes the low 32 bits of a 64-bit pair shifted right by 0..3 bytes).
+// A load that reaches past `end` can come back as zeros as a whole, so the chunks at the very end of
+// the operand are read an element at a time instead; elements past `end` read as zero.
+__device__ __forceinline__ u32x4 load16_unaligned(__amdgpu_buffer_rsrc_t r, unsigned off, unsigned end) {
+  const unsigned al = off & ~3u, sh = off & 3u;
+  u32x4 o;
+  if (al + 20u <= end) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, al, 0, 0);
+    const unsigned e = __builtin_amdgcn_raw_buffer_load_b32(r, al + 16u, 0, 0);
+    o[0] = __builtin_amdgcn_alignbyte(v[1], v[0], sh);
+    o[1] = __builtin_amdgcn_alignbyte(v[2], v[1], sh);
+    o[2] = __builtin_amdgcn_alignbyte(v[3], v[2], sh);
+    o[3] = __builtin_amdgcn_alignbyte(e, v[3], sh);
+  } else {
+    unsigned h[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) h[e] = k + e < g.K ? s[e] : (unsigned short)0;
-    u32x4 out;
+    for (int e = 0; e < 8; ++e)
+      h[e] = off + 2u * e + 2u <= end ? (unsigned)__builtin_amdgcn_raw_buffer_load_b16(r, off + 2u * e, 0, 0) : 0u;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) out[e] = (unsigned)h[2 * e] | ((unsigned)h[2 * e + 1] << 16);
-    unsigned short* d = (unsigned short*)(is_a ? g.dA : g.dB) + (size_t)row * g.ldd + k;
-    *(u32x4*)d = out;
+    for (int e = 0; e < 4; ++e) o[e] = h[2 * e] | (h[2 * e + 1] << 16);
   }
+  return o;
+}
+
+// One operand: dst rows of ldd = Kp elements (16-byte aligned) from src rows of ld elements (any
+// 2-byte alignment of the base and of ld): dst[row, k] = src[row, k] for k < K, 0 for K <= k < Kp.
+// Chunk q (8 elements) is chunk q mod cpr of row q / cpr (cpr = Kp / 8); the grid-stride loop starts
+// at chunk `first`. A is dealt from the first thread of the grid up and B from the last one down, so
+// the two share one launch and, when the grid holds both, no thread copies two chunks.
+__device__ __forceinline__ void stage_operand(const void* src, int ld, void* dst, int rows, int K, int ldd,
+                                              unsigned first, unsigned stride) {
+  const unsigned cpr = (unsigned)ldd >> 3;
+  const unsigned total = (unsigned)rows * cpr;
+  if (total == 0) return;
+  // the buffer starts at the dword holding src[0]; lead = 0 or 2 bytes before it
+  const uintptr_t base = (uintptr_t)src;
+  const unsigned lead = (unsigned)(base & 3u);
+  const unsigned end = lead + ((unsigned)(rows - 1) * (unsigned)ld + (unsigned)K) * 2u;  // < 2^31 (host check)
+  const __amdgpu_buffer_rsrc_t r = make_rsrc((const void*)(base - lead), end);
+  for (unsigned q = first; q < total; q += stride) {
+    const unsigned row = q / cpr;
+    const int k = (int)(8u * (q - row * cpr));
+    u32x4 out = load16_unaligned(r, lead + 2u * ((unsigned)row * (unsigned)ld + (unsigned)k), end);
+    if (k + 8 > K) {  // the K tail of the row: the padding columns are zero, whatever src holds there
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (k + e >= K) out[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+    }
+    *(u32x4*)((unsigned short*)dst + (size_t)row * ldd + k) = out;
+  }
+}
+
+__global__ void __launch_bounds__(256) stage_kernel(StageArgs g) {
+  const unsigned t = blockIdx.x * 256u + threadIdx.x, stride = gridDim.x * 256u;
+  stage_operand(g.A, g.lda, g.dA, g.rows_a, g.K, g.ldd, t, stride);
+  stage_operand(g.B, g.ldb, g.dB, g.rows_b, g.K, g.ldd, stride - 1u - t, stride);
 }
 
 const void* splitk_reduce_fn(int out_dtype) {

@@ -119,6 +119,18 @@ def test_config_choice(name):
         assert (c["bm"], c["bn"], c["bk"], c["stages"]) == (64, 64, 128, 4) and c["splits"] == 1
 
 
+def test_staging_needs_each_source_under_2gib():
+    # K = 7 rules out the DMA path. The staging copy reaches a source operand through 32-bit byte
+    # offsets: 2000 rows of lda = 600000 elements span 2.4 GB, so that plan takes the register path;
+    # 1000 rows (1.2 GB) stage as usual
+    c = spt.gemm_select_config(2000, 64, 7, F16, F16, F16, 600000, 7, 64, 256, 160 * 1024)
+    assert c["load_path"] == spt.GEMM_LOAD_REG
+    c = spt.gemm_select_config(1000, 64, 7, F16, F16, F16, 600000, 7, 64, 256, 160 * 1024)
+    assert c["load_path"] == spt.GEMM_LOAD_STAGED
+    c = spt.gemm_select_config(64, 2000, 7, F16, F16, F16, 7, 600000, 2000, 256, 160 * 1024)
+    assert c["load_path"] == spt.GEMM_LOAD_REG
+
+
 def test_two_part_choice():
     # 4093 x 5119 (K staged to 3072): 320 tiles of 256x256 for 256 workgroups, a second round a
     # quarter full. The plan cuts the columns at 4096 (16 x 16 tiles: one full round of the
