@@ -243,17 +243,22 @@ def clock(counter_csv: str, agent_csv: str, bench_json: str, out_md: str, comman
            f"Kernel: `{c['kernel']}`; {n_cu} CUs, {n_se} shader engines, peak engine clock {fmax / 1e9:.2f} GHz.",
            "clock = SQ_BUSY_CYCLES / shader engines / duration; MFMA utilisation = achieved flop rate / "
            "(CUs x 4096 flop/clk x clock).", "",
-           "| dispatch | duration (us) | TFLOP/s | clock (GHz) | MFMA util. at that clock | at peak clock | MFMA flop / 2MNK |",
-           "|---|---|---|---|---|---|---|"]
+           "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (4 SIMDs x CUs x clock x duration), the counter's own measure of",
+           "the same thing (empty where the pass did not collect it).", "",
+           "| dispatch | duration (us) | TFLOP/s | clock (GHz) | MFMA util. at that clock | MFMA busy | at peak clock | "
+           "MFMA flop / 2MNK |",
+           "|---|---|---|---|---|---|---|---|"]
     rows = []
     for i, (did, d) in enumerate(sorted(per.items())):
         mops = d.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) + d.get("SQ_INSTS_VALU_MFMA_MOPS_F16", 0.0)
         tf = flop_exact / d["dur"] / 1e12
         clk = d["SQ_BUSY_CYCLES"] / n_se / d["dur"]
         util = flop_exact / d["dur"] / (n_cu * 4096 * clk)
+        busy = d.get("SQ_VALU_MFMA_BUSY_CYCLES")
+        busy_s = f"{busy / (4 * n_cu * clk * d['dur']):.3f}" if busy is not None else ""
         rows.append((tf, clk, util))
         out.append(f"| {did}{' (first)' if i == 0 else ''} | {d['dur'] * 1e6:.1f} | {tf:.1f} | {clk / 1e9:.3f} | "
-                   f"{util:.3f} | {tf * 1e12 / (n_cu * 4096 * fmax):.3f} | {mops * 512 / flop_exact:.3f} |")
+                   f"{util:.3f} | {busy_s} | {tf * 1e12 / (n_cu * 4096 * fmax):.3f} | {mops * 512 / flop_exact:.3f} |")
     if len(rows) > 1:
         rest = rows[1:]
         out += ["", f"Mean over the launches after the first: {statistics.mean(r[0] for r in rest):.1f} TFLOP/s at "

@@ -302,6 +302,21 @@ def test_staged_operands_bit_exact(M, N, K, lda, ldb):
             check_full(a, b, K, in_dt, si.BF16, c, N, exact=True)
 
 
+def test_spans_beyond_2gib_sampled_exact():
+    # A spans 2.15 GB (16384 rows of lda = 65600) and the fp32 C 2.68 GB (16384 x 40960): tile base
+    # addresses lie past 2^31 bytes while each tile's own offsets stay below it. Integer inputs make
+    # every sampled output exact; the NaN sentinel shows any output left unwritten
+    M, N, K, lda = 16384, 40960, 64, 65600
+    a = ints(M, K, si.BF16, 77, ld=lda)
+    b = ints(N, K, si.BF16, 78)
+    c, desc = run_gpu(a, b, K, si.BF16, si.F32)
+    assert desc["load_path"] == spt.GEMM_LOAD_DMA
+    assert np.isfinite(c).all()
+    ii, jj = sample_indices(M, N, desc["bm"], desc["bn"], 4096, seed=5)
+    c_ref, _, _ = orc.gemm_sampled(a, b, K, si.BF16, si.F32, ii, jj)
+    assert np.array_equal(c[ii, jj].view(np.uint32), np.asarray(c_ref, dtype=np.float32).view(np.uint32))
+
+
 @pytest.mark.parametrize("K,lda", [(1024, 1024), (1023, 1023)])
 def test_two_part_plan_bit_exact(K, lda):
     # 4096 x 5119 at 256x256 is 16 x 20 = 320 tiles for 256 workgroups: the plan runs columns
