@@ -10,6 +10,10 @@
     ldsbw   LDS read bandwidth per CU: 8 waves per CU, 16 independent ds_read_b128 per wave in flight
     store   epilogue store shapes: rows per store instruction (16, 8, 4, 2) x lane layout, with 1, 8
             or 32 writing workgroups per XCD
+    ablation [c3|c4] the stage-count ablation: every tile and ring depth of the menu, persistent and
+            not, group_m 1 and the 32x32x16 MFMA form, each forced through the configuration override;
+            one untimed pass, then two alternating passes of 10 launches; prints a markdown table of
+            TFLOP/s
     library 8192^3 bf16 (N(0,1)/sqrt(K) inputs drawn with torch) through this library's default plan,
             its 4-wave 256x256 split-ring plan, and, for context only, torch.mm (the vendor GEMM
             library), in alternating blocks of launches; prints TFLOP/s per block. Run it under
@@ -129,6 +133,59 @@ def library(reps: int = 3, launches: int = 6) -> list[dict]:
     return rows
 
 
+ABLATION_SHAPES = {"c3": (8192, 8192, 8192, torch.bfloat16, "normal"),
+                   "c4": (16384, 16384, 1024, torch.bfloat16, "uniform")}
+# (row label, column label, tile, ring depth, waves, K-tile depth, load path, persistent, group_m, MFMA)
+ABLATION_ROWS = (
+    [("256x256 two-group (8 waves)", c, 256, 256, s, 8, 64, 1, p, g, m) for c, s, p, g, m in
+     (("S=2", 2, 1, 8, 16), ("S=5 (split ring)", 5, 1, 8, 16), ("non-persistent, S=5", 5, 0, 8, 16),
+      ("group_m = 1, S=5", 5, 1, 1, 16), ("32x32x16 MFMA, S=5", 5, 1, 8, 32))]
+    + [("256x256 4-wave", c, 256, 256, s, 4, 64, 1, p, 8, 16) for c, s, p in
+       (("S=1 (serial)", 1, 1), ("S=2", 2, 1), ("S=5 (split ring)", 5, 1), ("non-persistent, S=2", 2, 0))]
+    + [("256x128", c, 256, 128, s, 4, 64, 1, p, 8, 16) for c, s, p in
+       (("S=1 (serial)", 1, 1), ("S=2", 2, 1), ("S=3", 3, 1), ("non-persistent, S=3", 3, 0))]
+    + [("128x128", c, 128, 128, s, 4, 64, 1, p, 8, 16) for c, s, p in
+       (("S=1 (serial)", 1, 1), ("S=2", 2, 1), ("S=3", 3, 1), ("S=4", 4, 1), ("non-persistent, S=4", 4, 0))]
+    + [("128x128 register-staged", "S=2", 128, 128, 2, 4, 64, 2, 1, 8, 16)])
+
+
+def ablation(workload: str = "c3", passes: int = 2, launches: int = 10) -> str:
+    from .torch_api import Plan
+
+    M, N, K, dt, dist = ABLATION_SHAPES[workload]
+    g = torch.Generator(device="cuda").manual_seed(0)
+    if dist == "normal":
+        A = (torch.randn(M, K, device="cuda", generator=g) / K ** 0.5).to(dt)
+        B = (torch.randn(N, K, device="cuda", generator=g) / K ** 0.5).to(dt)
+    else:
+        A = (torch.rand(M, K, device="cuda", generator=g) * 2 - 1).to(dt)
+        B = (torch.rand(N, K, device="cuda", generator=g) * 2 - 1).to(dt)
+    C = torch.empty(M, N, dtype=dt, device="cuda")
+    sp = torch.cuda.current_stream().cuda_stream
+    plans = []
+    for row, col, bm, bn, s, w, bk, path, pers, gm, mf in ABLATION_ROWS:
+        cfg = dict(bm=bm, bn=bn, bk=bk, stages=s, waves=w, mfma=mf, persistent=pers, group_m=gm, load_path=path,
+                   grid=0, lds_bytes=0, splits=1)
+        plans.append((row, col, Plan(M, N, K, dt, dt, config=cfg)))
+    res = {(r, c): [] for r, c, _ in plans}
+    for _, _, p in plans:  # one untimed pass: clocks and caches settle before the first timed launch
+        for _ in range(launches):
+            p.run_ptrs(A.data_ptr(), B.data_ptr(), C.data_ptr(), sp)
+    torch.cuda.synchronize()
+    for _ in range(passes):
+        for r, c, p in plans:
+            p.run_ptrs(A.data_ptr(), B.data_ptr(), C.data_ptr(), sp)
+            ms, _ = _timed(lambda p=p: [p.run_ptrs(A.data_ptr(), B.data_ptr(), C.data_ptr(), sp)
+                                        for _ in range(launches)])
+            res[(r, c)].append(2.0 * M * N * K * launches / (ms * 1e-3) / 1e12)
+    for _, _, p in plans:
+        p.close()
+    out = [f"| {workload}: configuration | TFLOP/s (one per pass) |", "|---|---|"]
+    for (r, c), v in res.items():
+        out.append(f"| {r}, {c} | " + " / ".join(f"{x:.0f}" for x in v) + " |")
+    return "\n".join(out)
+
+
 def lds(iters: int = 2000) -> None:
     for sw in (-1, 0, 1, 2, 3, 4):
         _lib.gemm_probe_lds_read(sw, iters)
@@ -151,6 +208,8 @@ if __name__ == "__main__":
             print(row)
     elif what == "ldsbw":
         print(ldsbw())
+    elif what == "ablation":
+        print(ablation(sys.argv[2] if len(sys.argv) > 2 else "c3"), flush=True)
     elif what == "library":
         for row in library():
             print(row, flush=True)
