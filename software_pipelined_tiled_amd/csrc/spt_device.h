@@ -195,9 +195,12 @@ __device__ __forceinline__ void store8(const float (&v)[8], __amdgpu_buffer_rsrc
   }
 }
 
+// Cache-policy operand of a buffer store that marks the data non-temporal (the nt bit on gfx950).
+constexpr int kStoreNonTemporal = 2;
+
 // Store the 8 consecutive outputs v[0..7] at byte offset voffset + soffset of `rc` (an interior
-// segment: no masking).
-template <int OUT>
+// segment: no masking), with cache policy CPOL (0, or kStoreNonTemporal).
+template <int OUT, int CPOL = 0>
 __device__ __forceinline__ void store8_at(const float (&v)[8], __amdgpu_buffer_rsrc_t rc, unsigned voffset,
                                          unsigned soffset) {
   if constexpr (OUT == 2) {
@@ -205,14 +208,14 @@ __device__ __forceinline__ void store8_at(const float (&v)[8], __amdgpu_buffer_r
                 __builtin_bit_cast(unsigned, v[2]), __builtin_bit_cast(unsigned, v[3])};
     u32x4 hi = {__builtin_bit_cast(unsigned, v[4]), __builtin_bit_cast(unsigned, v[5]),
                 __builtin_bit_cast(unsigned, v[6]), __builtin_bit_cast(unsigned, v[7])};
-    __builtin_amdgcn_raw_buffer_store_b128(lo, rc, voffset, soffset, 0);
-    __builtin_amdgcn_raw_buffer_store_b128(hi, rc, voffset, soffset + 16u, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(lo, rc, voffset, soffset, CPOL);
+    __builtin_amdgcn_raw_buffer_store_b128(hi, rc, voffset, soffset + 16u, CPOL);
   } else {
     unsigned p[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) p[e] = OUT == 1 ? pack_bf16(v[2 * e], v[2 * e + 1]) : pack_f16(v[2 * e], v[2 * e + 1]);
     u32x4 q = {p[0], p[1], p[2], p[3]};
-    __builtin_amdgcn_raw_buffer_store_b128(q, rc, voffset, soffset, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(q, rc, voffset, soffset, CPOL);
   }
 }
 

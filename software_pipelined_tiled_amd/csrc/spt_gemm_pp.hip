@@ -315,10 +315,15 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmArgs args) {
     const int m_lane = MF == 16 ? m_base + 4 * (ln / 16) : m_base + ln % MF;
     const int n_lane = MF == 16 ? tl.col0 + TN * wn + 8 * (ln % 16) : tl.col0 + TN * wn + 8 * (ln / MF);
     const bool full = tl.rows_left >= BM && tl.cols_left >= BN;
+    // A finished output tile is not read again by this launch: its interior stores go out
+    // non-temporal (measured 1-2 % faster on 4096^3 .. 16384^2 x 1024). Split-K partial planes, which
+    // the reduction reads back next, keep the default policy (1.4 % slower non-temporal).
+    const bool nt = args.splits == 1;
     const unsigned voff = (unsigned)(m_lane * args.ldc + n_lane) * (unsigned)es;
     // 8 consecutive outputs at (m_lane + dm, n_lane + dn)
     auto put8 = [&](const float (&vv)[8], int dm, int dn) SPT_INLINE {
-      if (full) store8_at<OUT>(vv, rc, voff, (unsigned)((dm * args.ldc + dn) * es));
+      if (full && nt) store8_at<OUT, kStoreNonTemporal>(vv, rc, voff, (unsigned)((dm * args.ldc + dn) * es));
+      else if (full) store8_at<OUT>(vv, rc, voff, (unsigned)((dm * args.ldc + dn) * es));
       else store8<OUT, true>(vv, rc, m_lane + dm, tl.rows_left, n_lane + dn, N, args.ldc);
       __builtin_amdgcn_sched_barrier(0);
     };
