@@ -5,13 +5,15 @@ Default workload: M = N = K = 8192, bf16 inputs drawn N(0,1)/sqrt(K), fp32 accum
 output. One step is one gemm_run over operands already resident in HBM. Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--shape-index I]
-                    [--config JSON] [--no-cpu-baseline] [--copy-calibration] [--cold]
+                    [--config JSON] [--no-cpu-baseline] [--copy-calibration] [--cold] [--graph]
 
 The roofline object names the bound of the workload: "mfma" (TFLOP/s against the dense peak) when
 2MNK at the MFMA peak takes longer than the compulsory bytes at 8 TB/s, else "hbm" (compulsory GB/s
 against 8 TB/s). A plan that splits K or stages its operands launches more than one kernel per run;
 the per-launch time is then that of the whole run (mainloop plus reduction or staging copy).
 With --cold, B rotates over enough copies that the 256 MB MALL cannot hold them, so B comes from HBM.
+With --graph, the K timed launches are captured once in a HIP graph and replayed, so a step costs no host
+launch (this matters only for the smallest problems, whose kernels are shorter than a launch from Python).
 """
 from __future__ import annotations
 
@@ -84,6 +86,8 @@ def main() -> int:
                     help="also launch one 1 GiB copy kernel (reference for memory-traffic counters)")
     ap.add_argument("--no-probes", action="store_true", help="skip the MFMA-peak and HBM-copy probes")
     ap.add_argument("--cold", action="store_true", help="rotate B over copies that together exceed the MALL")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture the K timed launches in one HIP graph and replay it (no host launch cost per step)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -122,12 +126,25 @@ def main() -> int:
     # the timed region: K launches back to back between two events on the stream they run on. The
     # mean launch time is taken over this region too: an event pair around every launch adds a few
     # microseconds per step, several percent of a short launch
+    graph = None
+    if args.graph:
+        # the same K launches recorded once and replayed as one graph: a step then costs the GPU's time
+        # alone, where a launch from the host loop can cost more than a small problem's kernel
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            cap = torch.cuda.current_stream().cuda_stream
+            for i in range(args.steps):
+                plan.run_ptrs(A.data_ptr(), b_copies[i % len(b_copies)].data_ptr(), C.data_ptr(), cap)
+        graph.replay()  # one untimed replay
     all_start, all_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     all_start.record(stream)
-    for i in range(args.steps):
-        plan.run_ptrs(A.data_ptr(), b_copies[i % len(b_copies)].data_ptr(), C.data_ptr(), sp)
+    if graph is not None:
+        graph.replay()
+    else:
+        for i in range(args.steps):
+            plan.run_ptrs(A.data_ptr(), b_copies[i % len(b_copies)].data_ptr(), C.data_ptr(), sp)
     all_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -189,7 +206,8 @@ def main() -> int:
                    "out_dtype": DTYPE_NAME[out_dt], "accumulate": "f32",
                    "distribution": si.WORKLOADS[args.workload]["dist"], "kernel": kernel_name, "plan": desc,
                    **({"parts": parts} if parts["dim"] >= 0 else {}),
-                   "b_cache": "cold (rotated copies)" if args.cold else "warm"},
+                   "b_cache": "cold (rotated copies)" if args.cold else "warm",
+                   "launch": "hip graph replay" if args.graph else "host loop"},
         "roofline": ({"bound": "hbm", "achieved": compulsory / (avg_launch_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
                       "unit": "GB/s", "frac": compulsory / (avg_launch_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
                       "traffic": traffic} if hbm_bound else

@@ -25,7 +25,7 @@ if not torch.cuda.is_available():  # collected on CPU-only hosts, never run ther
     pytest.skip("needs a GPU", allow_module_level=True)
 
 import software_pipelined_tiled_amd as spt  # noqa: E402
-from gpu_helpers import check_full, check_sampled, run_gpu, sample_indices  # noqa: E402
+from gpu_helpers import check_full, check_sampled, run_gpu, sample_indices, to_device  # noqa: E402
 
 DMA_CONFIGS = [(256, 256, 2), (256, 256, 1), (256, 128, 3), (256, 128, 2), (256, 128, 1), (128, 128, 4),
                (128, 128, 3), (128, 128, 2), (128, 128, 1), (64, 64, 4), (64, 64, 2)]
@@ -300,6 +300,43 @@ def test_staged_operands_bit_exact(M, N, K, lda, ldb):
             c, desc = run_gpu(a, b, K, in_dt, si.BF16, config=conf, a_off=1, b_off=3)
             assert desc["load_path"] == spt.GEMM_LOAD_STAGED
             check_full(a, b, K, in_dt, si.BF16, c, N, exact=True)
+
+
+@pytest.mark.parametrize("shape,config,lda", [
+    ((256, 256, 256), None, None),                                      # one kernel (deep 64x64 tile)
+    ((300, 260, 648), cfg(64, 64, 4, splits=3), None),                  # mainloop + reduction
+    ((200, 130, 77), None, 77),                                         # staging copy + mainloop
+    ((4096, 5119, 1024), None, None),                                   # two parts, two mainloops
+])
+def test_graph_replay_matches_eager(shape, config, lda):
+    # gemm_run captured in a HIP graph and replayed three times, with eager work of the same plan and
+    # synchronisations in between; every replay must equal the eager result bit for bit
+    M, N, K = shape
+    a = ints(M, K, si.F16, 61 + K, ld=lda)
+    b = ints(N, K, si.F16, 62 + K, ld=lda)
+    A = to_device(a, si.F16)
+    B = to_device(b, si.F16)
+    plan = spt.Plan(M, N, K, torch.float16, torch.float32, a.shape[1], b.shape[1], N, config)
+    C_eager = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    C_graph = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    C_other = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    plan.run_ptrs(A.data_ptr(), B.data_ptr(), C_eager.data_ptr())
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        plan.run_ptrs(A.data_ptr(), B.data_ptr(), C_graph.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    want = C_eager.cpu()
+    for rep in range(3):
+        C_graph.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(C_graph.cpu().view(torch.int32), want.view(torch.int32)), f"replay {rep}"
+        plan.run_ptrs(A.data_ptr(), B.data_ptr(), C_other.data_ptr())  # eager work between replays
+        torch.cuda.synchronize()
+    plan.close()
+    if M * N * K <= 1 << 26:  # the eager result itself, against the oracle (other tests cover the large plan)
+        check_full(a, b, K, si.F16, si.F32, want.numpy(), N, exact=True)
 
 
 def test_spans_beyond_2gib_sampled_exact():
