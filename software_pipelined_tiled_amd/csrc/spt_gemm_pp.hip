@@ -113,8 +113,8 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmArgs args) {
   const int u0 = xcd_remap(blockIdx.x, args.grid);
   // The workgroups of XCD x take the K-tiles of every unit in a rotated order, starting at K-tile
   // x*KT/8: all workgroups of one XCD stay at the same K position (their L2 sharing is unchanged),
-  // while the eight XCDs reach their epilogues at different times, so the output stores of the
-  // chip do not all fall into the same phase. Only the summation order changes.
+  // while at any moment the eight XCDs fetch eight different K-slices of the operand bands rather
+  // than the same addresses at once. Only the summation order changes; the epilogues do not move.
   const int krot = (int)((blockIdx.x % kNumXcd) * KT / kNumXcd);
   auto ktile = [&](int u) SPT_INLINE {
     const int r = u + krot;
