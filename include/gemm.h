@@ -76,7 +76,14 @@ typedef enum {
  *                the other issues loads, alternating at workgroup barriers
  *   mfma         MFMA shape: 16 = v_mfma_f32_16x16x32_{f16,bf16}; 32 = v_mfma_f32_32x32x16_{f16,bf16}
  *                (two-wave-group kernel with the split ring only: 256x256, bk 64, stages 5, waves 8)
- *   persistent   1: launch min(#tiles, grid) workgroups that loop over tiles; 0: one per tile
+ *   persistent   1: launch min(#tiles, grid) workgroups that loop over tiles in static rounds;
+ *                0: one workgroup per tile; 2: as 1, but after its first tile each workgroup takes
+ *                the next tile nobody has taken from an atomic counter in the plan's workspace
+ *                (4-wave DMA kernels whose ring leaves 16 bytes of the 160 KiB of LDS, else
+ *                GEMM_ERR_UNSUPPORTED). The counters are zero
+ *                when a launch starts and the launch leaves them at zero, so the plan needs no
+ *                reset between runs or graph replays; like every plan with a workspace it must
+ *                not run on two streams at once
  *   group_m      grouped raster height, in tiles (tiles sharing A row bands run back to back)
  *   load_path    gemm_load_path_t
  *   grid         workgroups launched (describe only; 0 in an override means "from the device")

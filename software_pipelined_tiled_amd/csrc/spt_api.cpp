@@ -25,6 +25,7 @@ struct gemm_plan_s {
   char* ws;
   int64_t kp;              // K as the mainloop sees it: K, or K rounded up to 8 when staged
   int64_t stage_a_off, stage_b_off, part_off;  // byte offsets inside ws
+  int64_t queue_off;       // the dynamic schedule's two counters (persistent 2), inside ws
   int64_t ldw;             // row length of a partial plane (elements)
   const void* fn_reduce;
   const void* fn_stage;
@@ -51,11 +52,12 @@ int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 bool is_dma(int path) { return path == GEMM_LOAD_DMA || path == GEMM_LOAD_STAGED; }
 
 // Workspace layout: staged A (M rows of kp elements), staged B (N rows), then `splits` fp32 planes
-// of M rows of ldw = N rounded up to 8 elements; each part starts on a 256-byte boundary.
+// of M rows of ldw = N rounded up to 8 elements, then, for a dynamic schedule, the two queue
+// counters; each part starts on a 256-byte boundary.
 struct WsLayout {
-  int64_t stage_a, stage_b, part, total, kp, ldw;
+  int64_t stage_a, stage_b, part, queue, total, kp, ldw;
 };
-WsLayout ws_layout(int64_t M, int64_t N, int64_t K, int path, int splits) {
+WsLayout ws_layout(int64_t M, int64_t N, int64_t K, int path, int splits, bool queue = false) {
   WsLayout w{};
   const bool staged = path == GEMM_LOAD_STAGED;
   w.kp = staged ? round_up(K, 8) : K;
@@ -65,7 +67,9 @@ WsLayout ws_layout(int64_t M, int64_t N, int64_t K, int path, int splits) {
   w.stage_a = 0;
   w.stage_b = a_bytes;
   w.part = a_bytes + b_bytes;
-  w.total = w.part + (splits > 1 ? (int64_t)splits * M * w.ldw * 4 : 0);
+  const int64_t planes_end = w.part + (splits > 1 ? (int64_t)splits * M * w.ldw * 4 : 0);
+  w.queue = round_up(planes_end, 256);
+  w.total = queue ? w.queue + 256 : planes_end;
   return w;
 }
 int64_t stage_bytes(int64_t M, int64_t N, int64_t K) { return ws_layout(M, N, K, GEMM_LOAD_STAGED, 1).total; }
@@ -307,6 +311,7 @@ void finish_config(gemm_config_t& c, int64_t M, int64_t N, int cu_count, int lds
 
 gemm_status_t validate_override(const gemm_config_t& c) {
   if (c.mfma != 16 && c.mfma != 32 && c.mfma != 0) return GEMM_ERR_INVALID;
+  if (c.persistent < 0 || c.persistent > 2) return GEMM_ERR_INVALID;
   if (c.load_path < GEMM_LOAD_AUTO || c.load_path > GEMM_LOAD_STAGED) return GEMM_ERR_INVALID;
   if (c.group_m < 0 || c.grid < 0) return GEMM_ERR_INVALID;
   if (c.splits < 0 || c.splits > kMaxSplits) return GEMM_ERR_INVALID;
@@ -338,6 +343,9 @@ gemm_status_t select_impl(int64_t M, int64_t N, int64_t K, gemm_dtype_t a, gemm_
     cfg.lds_bytes = ring_bytes(cfg);
     if (!find_entry_for_path(cfg)) return GEMM_ERR_INVALID;
     if (cfg.lds_bytes > lds_bytes) return GEMM_ERR_INVALID;
+    // the dynamic queue is built into the 4-wave DMA kernel, for rings that leave it 16 bytes of LDS
+    if (cfg.persistent == 2 && (cfg.waves == 8 || cfg.load_path == GEMM_LOAD_REG || cfg.lds_bytes + 16 > kMaxLds))
+      return GEMM_ERR_UNSUPPORTED;
   } else if (dma_ok) {
     cfg = choose(M, N, K, kDmaMenu, kDmaMenuSize, GEMM_LOAD_DMA, cu_count, lds_bytes);
   } else if (stage_ok) {
@@ -415,6 +423,7 @@ gemm_status_t gemm_plan_create(gemm_plan_t* out, int64_t M, int64_t N, int64_t K
   p->in_dtype = a_dtype; p->out_dtype = c_dtype;
   p->dev = dev;
   p->split_dim = -1;
+  p->queue_off = -1;
   st = select_impl(M, N, K, a_dtype, b_dtype, c_dtype, lda, ldb, ldc, cu, lds, config, &p->cfg, &p->cfg_reg);
   if (st != GEMM_OK) { delete p; return st; }
   // the built-in choice may cut the output in two (wave quantisation); each part is a plan over
@@ -449,7 +458,9 @@ gemm_status_t gemm_plan_create(gemm_plan_t* out, int64_t M, int64_t N, int64_t K
   p->tiles_m_reg = (int)ceil_div(M, p->cfg_reg.bm);
   p->tiles_n_reg = (int)ceil_div(N, p->cfg_reg.bn);
   if (!p->fn_main) { delete p; return GEMM_ERR_UNSUPPORTED; }
-  const WsLayout w = ws_layout(M, N, K, p->cfg.load_path, p->split_dim >= 0 ? 1 : p->cfg.splits);
+  const WsLayout w = ws_layout(M, N, K, p->cfg.load_path, p->split_dim >= 0 ? 1 : p->cfg.splits,
+                               p->split_dim < 0 && p->cfg.persistent == 2);
+  p->queue_off = p->split_dim < 0 && p->cfg.persistent == 2 ? w.queue : -1;
   p->kp = w.kp;
   p->ldw = w.ldw;
   p->stage_a_off = w.stage_a;
@@ -465,6 +476,12 @@ gemm_status_t gemm_plan_create(gemm_plan_t* out, int64_t M, int64_t N, int64_t K
       return GEMM_ERR_NOMEM;
     }
     p->ws = (char*)ws;
+    // the queue counters start at zero; each launch leaves them at zero again
+    if (p->queue_off >= 0 && hipMemset(p->ws + p->queue_off, 0, 8) != hipSuccess) {
+      (void)hipGetLastError();
+      (void)gemm_plan_destroy(p);
+      return GEMM_ERR_HIP;
+    }
   }
   *out = p;
   return GEMM_OK;
@@ -538,7 +555,8 @@ gemm_status_t gemm_select_parts(int64_t M, int64_t N, int64_t K, gemm_dtype_t a_
 
 gemm_status_t gemm_plan_workspace_bytes(gemm_plan_t plan, int64_t* out) {
   if (!plan || !out) return GEMM_ERR_INVALID;
-  *out = plan->ws ? ws_layout(plan->M, plan->N, plan->K, plan->cfg.load_path, plan->split_dim >= 0 ? 1 : plan->cfg.splits).total
+  *out = plan->ws ? ws_layout(plan->M, plan->N, plan->K, plan->cfg.load_path, plan->split_dim >= 0 ? 1 : plan->cfg.splits,
+                              plan->queue_off >= 0).total
                  : 0;
   for (gemm_plan_s* part : plan->part) {
     int64_t b = 0;
@@ -618,6 +636,7 @@ gemm_status_t gemm_run(gemm_plan_t plan, const void* A, const void* B, void* C, 
   args.splits = splits;
   args.kt_per = (int)ceil_div(ceil_div(K, cfg->bk), splits);
   args.split_stride = 0;
+  args.queue = cfg == &plan->cfg && plan->queue_off >= 0 ? (int*)(plan->ws + plan->queue_off) : nullptr;
   if (splits > 1) {
     args.C = plan->ws + plan->part_off;
     args.ldc = (int)plan->ldw;

@@ -118,6 +118,10 @@ struct GemmArgs {
   int splits;     // K ranges per output tile (1: the whole K in one unit)
   int kt_per;     // K-tiles per work unit
   long long split_stride;  // bytes from the partial plane of K range s to that of s + 1
+  // Dynamic schedule (4-wave kernel only): null for the static rounds. Else two counters in the
+  // plan's workspace, zero at launch: [0] hands out the units after each workgroup's first one,
+  // [1] counts finished workgroups; the last workgroup to finish sets both back to zero.
+  int* queue;
 };
 
 }  // namespace spt

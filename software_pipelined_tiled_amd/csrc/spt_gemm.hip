@@ -31,7 +31,10 @@ struct Regions {
 template <int BM, int BN, int BK, int S, int WM, int WN, typename TIn, int OUT>
 __global__ void __launch_bounds__(WM* WN * 64, 1) gemm_dma_kernel(GemmArgs args) {
   using T = TileShape<BM, BN, BK, S, WM, WN>;
-  __shared__ __attribute__((aligned(1024))) char smem[T::LDS];
+  // 16 bytes past the ring hold the dynamic schedule's next unit, where the ring leaves room for them
+  // (the host enables the queue only for those configurations)
+  constexpr int kQueueSlot = T::LDS + 16 <= 160 * 1024 ? 16 : 0;
+  __shared__ __attribute__((aligned(1024))) char smem[T::LDS + kQueueSlot];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -82,7 +85,25 @@ __global__ void __launch_bounds__(WM* WN * 64, 1) gemm_dma_kernel(GemmArgs args)
 
   const int u = xcd_remap(blockIdx.x, args.grid);
   bool first_tile = true;
-  for (int t = u; t < args.num_tiles; t += args.grid) {
+  // The next work unit: the static schedule's next round, or, with a queue, the next unit nobody has
+  // taken yet (every workgroup's first unit is its static one). One lane takes it with an atomic
+  // add and hands it to the other waves through LDS; the second barrier keeps the slot from being
+  // overwritten before every wave has read it. Each unit is handed out once, so every workgroup
+  // ends its loop after at most num_tiles takes.
+  auto next = [&](int t) {
+    if constexpr (kQueueSlot == 0) {
+      return t + args.grid;
+    } else {
+      if (args.queue == nullptr) return t + args.grid;
+      int* const slot = (int*)(smem + T::LDS);
+      if (threadIdx.x == 0) *slot = args.grid + atomicAdd(&args.queue[0], 1);
+      barrier_sync();
+      const int n = *slot;
+      barrier_sync();
+      return n;
+    }
+  };
+  for (int t = u; t < args.num_tiles; t = next(t)) {
     int tm, tn, ks;
     unit_decode(t, args.tiles_m, args.tiles_n, args.group_m, tm, tn, ks);
     const int row0 = tm * BM, col0 = tn * BN;
@@ -340,6 +361,13 @@ __global__ void __launch_bounds__(WM* WN * 64, 1) gemm_dma_kernel(GemmArgs args)
     };
     if (full_tile) epilogue(std::false_type{});
     else epilogue(std::true_type{});
+  }
+  if (kQueueSlot != 0 && args.queue != nullptr && threadIdx.x == 0) {
+    // this workgroup takes no more units; the last one to get here resets the queue for the next launch
+    if (atomicAdd(&args.queue[1], 1) == args.grid - 1) {
+      atomicExch(&args.queue[0], 0);
+      atomicExch(&args.queue[1], 0);
+    }
   }
 }
 

@@ -91,6 +91,49 @@ def test_ring_configs_k_around_depth(K, bk, s, waves):
     check_full(a, b, K, si.BF16, si.F32, c, N, exact=True)
 
 
+# (bm, bn, bk, stages) of 4-wave configurations whose ring leaves room for the dynamic queue's slot
+QUEUE_CONFIGS = [(256, 256, 64, 2), (256, 128, 64, 3), (128, 128, 64, 4), (64, 64, 64, 4), (64, 64, 128, 4)]
+
+
+@pytest.mark.parametrize("bm,bn,bk,s", QUEUE_CONFIGS)
+@pytest.mark.parametrize("splits", [1, 3])
+def test_dynamic_queue_bit_exact(bm, bn, bk, s, splits):
+    # persistent = 2: after its first unit each workgroup takes the next free one from an atomic
+    # counter. Three workgroups over a ragged 3 x 2 grid (times the K ranges) take many units each;
+    # three launches in a row check that each launch leaves the counters at zero for the next
+    M, N, K = 2 * bm + bm // 2 + 3, 2 * bn - 5, 9 * bk + 24
+    a = ints(M, K, si.BF16, 700 + bm + s + splits)
+    b = ints(N, K, si.BF16, 800 + bn + bk + splits)
+    A, B = to_device(a, si.BF16), to_device(b, si.BF16)
+    conf = cfg(bm, bn, s, bk=bk, persistent=2, grid=3, splits=splits)
+    plan = spt.Plan(M, N, K, torch.bfloat16, torch.float32, K, K, N, conf)
+    desc = plan.describe()
+    assert desc["persistent"] == 2 and desc["grid"] == 3 and desc["splits"] == splits
+    assert plan.workspace_bytes() > 0
+    ref = None
+    for run in range(3):
+        C = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+        plan.run_ptrs(A.data_ptr(), B.data_ptr(), C.data_ptr())
+        torch.cuda.synchronize()
+        got = C.cpu().numpy()
+        if ref is None:
+            check_full(a, b, K, si.BF16, si.F32, got, N, exact=True)
+            ref = got
+        assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), f"run {run}"
+    plan.close()
+
+
+def test_dynamic_queue_rejected_where_not_built():
+    M = N = K = 512
+    for conf, status in ((ring_cfg(64, 5, 8, persistent=2), spt._lib.GEMM_ERR_UNSUPPORTED),   # two-group kernel
+                         (ring_cfg(64, 5, 4, persistent=2), spt._lib.GEMM_ERR_UNSUPPORTED),   # ring fills the LDS
+                         (cfg(128, 128, 2, path=spt.GEMM_LOAD_REG, persistent=2), spt._lib.GEMM_ERR_UNSUPPORTED),
+                         (cfg(128, 128, 4, persistent=3), spt._lib.GEMM_ERR_INVALID)):
+        with pytest.raises(spt.GemmError) as e:
+            spt.Plan(M, N, K, torch.float16, torch.float16, config=conf)
+        assert e.value.status == status, conf
+
+
 @pytest.mark.parametrize("K", [8, 120, 128, 136, 384, 512, 520, 5 * 128 + 24])
 @pytest.mark.parametrize("persistent", [1, 0])
 def test_deep_64_tile_bit_exact(K, persistent):
@@ -307,6 +350,7 @@ def test_staged_operands_bit_exact(M, N, K, lda, ldb):
     ((300, 260, 648), cfg(64, 64, 4, splits=3), None),                  # mainloop + reduction
     ((200, 130, 77), None, 77),                                         # staging copy + mainloop
     ((4096, 5119, 1024), None, None),                                   # two parts, two mainloops
+    ((700, 500, 648), cfg(128, 128, 4, persistent=2, grid=5), None),    # dynamic unit queue
 ])
 def test_graph_replay_matches_eager(shape, config, lda):
     # gemm_run captured in a HIP graph and replayed three times, with eager work of the same plan and
