@@ -317,8 +317,10 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmArgs args) {
     const bool full = tl.rows_left >= BM && tl.cols_left >= BN;
     // A finished output tile is not read again by this launch: its interior stores go out
     // non-temporal (measured 1-2 % faster on 4096^3 .. 16384^2 x 1024). Split-K partial planes, which
-    // the reduction reads back next, keep the default policy (1.4 % slower non-temporal).
-    const bool nt = args.splits == 1;
+    // the reduction reads back next, keep the default policy (1.4 % slower non-temporal), and so do
+    // the MF = 32 stores, whose quarter-waves cover 16 rows of 16 bytes rather than whole 128-byte
+    // lines (non-temporal, 16384^2 x 1024 ran 30 % slower).
+    const bool nt = MF == 16 && args.splits == 1;
     const unsigned voff = (unsigned)(m_lane * args.ldc + n_lane) * (unsigned)es;
     // 8 consecutive outputs at (m_lane + dm, n_lane + dn)
     auto put8 = [&](const float (&vv)[8], int dm, int dn) SPT_INLINE {

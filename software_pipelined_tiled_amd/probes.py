@@ -10,8 +10,9 @@
     ldsbw   LDS read bandwidth per CU: 8 waves per CU, 16 independent ds_read_b128 per wave in flight
     store   epilogue store shapes: rows per store instruction (16, 8, 4, 2) x lane layout, with 1, 8
             or 32 writing workgroups per XCD
-    ablation [c3|c4] the stage-count ablation: every tile and ring depth of the menu, persistent and
-            not, group_m 1 and the 32x32x16 MFMA form, each forced through the configuration override;
+    ablation [c3|c4] the stage-count ablation: every tile and ring depth of the menu, persistent (static
+            rounds or the dynamic queue) and not, group_m 1 and the 32x32x16 MFMA form, each forced
+            through the configuration override;
             one untimed pass, then two alternating passes of 10 launches; prints a markdown table of
             TFLOP/s
     library 8192^3 bf16 (N(0,1)/sqrt(K) inputs drawn with torch) through this library's default plan,
@@ -143,9 +144,11 @@ ABLATION_ROWS = (
     + [("256x256 4-wave", c, 256, 256, s, 4, 64, 1, p, 8, 16) for c, s, p in
        (("S=1 (serial)", 1, 1), ("S=2", 2, 1), ("S=5 (split ring)", 5, 1), ("non-persistent, S=2", 2, 0))]
     + [("256x128", c, 256, 128, s, 4, 64, 1, p, 8, 16) for c, s, p in
-       (("S=1 (serial)", 1, 1), ("S=2", 2, 1), ("S=3", 3, 1), ("non-persistent, S=3", 3, 0))]
+       (("S=1 (serial)", 1, 1), ("S=2", 2, 1), ("S=3", 3, 1), ("non-persistent, S=3", 3, 0),
+        ("dynamic queue, S=3", 3, 2))]
     + [("128x128", c, 128, 128, s, 4, 64, 1, p, 8, 16) for c, s, p in
-       (("S=1 (serial)", 1, 1), ("S=2", 2, 1), ("S=3", 3, 1), ("S=4", 4, 1), ("non-persistent, S=4", 4, 0))]
+       (("S=1 (serial)", 1, 1), ("S=2", 2, 1), ("S=3", 3, 1), ("S=4", 4, 1), ("non-persistent, S=4", 4, 0),
+        ("dynamic queue, S=4", 4, 2))]
     + [("128x128 register-staged", "S=2", 128, 128, 2, 4, 64, 2, 1, 8, 16)])
 
 
