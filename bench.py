@@ -91,8 +91,8 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures a single GPU: runs with --gpus N for N > 1 are not supported by this build",
-              file=sys.stderr)
+        print("bench.py measures one GPU: the library runs each GEMM on a single device, so --gpus N with N > 1 "
+              "is not supported", file=sys.stderr)
         return 2
 
     import numpy as np
