@@ -15,8 +15,9 @@
             through the configuration override;
             one untimed pass, then two alternating passes of 10 launches; prints a markdown table of
             TFLOP/s
-    library 8192^3 bf16 (N(0,1)/sqrt(K) inputs drawn with torch) through this library's default plan,
-            its 4-wave 256x256 split-ring plan, and, for context only, torch.mm (the vendor GEMM
+    library [c3|c4|c2|c5a|c5b|c5c [launches]] one workload (8192^3 bf16 by default, inputs drawn with
+            torch in the workload's distribution) through this library's default plan (for 8192^3
+            also its 4-wave 256x256 split-ring plan) and, for context only, torch.mm (the vendor GEMM
             library), in alternating blocks of launches; prints TFLOP/s per block. Run it under
             rocprofv3 --pmc to compare clock, MFMA utilisation and instruction mix per kernel.
 """
@@ -109,18 +110,31 @@ def ldsbw(iters: int = 4000) -> dict:
             "TB_per_s_total": nbytes / (ms * 1e-3) / 1e12}
 
 
-def library(reps: int = 3, launches: int = 6) -> list[dict]:
+LIBRARY_SHAPES = {"c3": (8192, 8192, 8192, torch.bfloat16, "normal"),
+                  "c4": (16384, 16384, 1024, torch.bfloat16, "uniform"),
+                  "c2": (4096, 4096, 4096, torch.float16, "uniform"),
+                  "c5a": (32, 8192, 8192, torch.float16, "uniform"),
+                  "c5b": (4093, 5119, 3071, torch.float16, "uniform"),
+                  "c5c": (8192, 1024, 28672, torch.float16, "uniform")}
+
+
+def library(workload: str = "c3", reps: int = 3, launches: int = 6) -> list[dict]:
     from .torch_api import Plan
 
-    M = N = K = 8192
+    M, N, K, dt, dist = LIBRARY_SHAPES[workload]
     g = torch.Generator(device="cuda").manual_seed(0)
-    A = (torch.randn(M, K, device="cuda", generator=g) / K ** 0.5).to(torch.bfloat16)
-    B = (torch.randn(N, K, device="cuda", generator=g) / K ** 0.5).to(torch.bfloat16)
-    C = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
-    four_wave = dict(bm=256, bn=256, bk=64, stages=5, waves=4, mfma=16, persistent=1, group_m=8, load_path=1,
-                     grid=0, lds_bytes=0, splits=1)
-    plans = {"default plan": Plan(M, N, K, torch.bfloat16, torch.bfloat16),
-             "4-wave split ring": Plan(M, N, K, torch.bfloat16, torch.bfloat16, config=four_wave)}
+    if dist == "normal":
+        A = (torch.randn(M, K, device="cuda", generator=g) / K ** 0.5).to(dt)
+        B = (torch.randn(N, K, device="cuda", generator=g) / K ** 0.5).to(dt)
+    else:
+        A = (torch.rand(M, K, device="cuda", generator=g) * 2 - 1).to(dt)
+        B = (torch.rand(N, K, device="cuda", generator=g) * 2 - 1).to(dt)
+    C = torch.empty(M, N, dtype=dt, device="cuda")
+    plans = {"default plan": Plan(M, N, K, dt, dt)}
+    if workload == "c3":
+        four_wave = dict(bm=256, bn=256, bk=64, stages=5, waves=4, mfma=16, persistent=1, group_m=8, load_path=1,
+                         grid=0, lds_bytes=0, splits=1)
+        plans["4-wave split ring"] = Plan(M, N, K, dt, dt, config=four_wave)
     sp = torch.cuda.current_stream().cuda_stream
     runs = {name: (lambda p=p: p.run_ptrs(A.data_ptr(), B.data_ptr(), C.data_ptr(), sp)) for name, p in plans.items()}
     runs["torch.mm (context)"] = lambda: torch.mm(A, B.t(), out=C)
@@ -128,7 +142,8 @@ def library(reps: int = 3, launches: int = 6) -> list[dict]:
     for r in range(reps):
         for name, fn in runs.items():
             ms, _ = _timed(lambda: [fn() for _ in range(launches)])
-            rows.append({"rep": r, "kernel": name, "TFLOP/s": 2.0 * M * N * K * launches / (ms * 1e-3) / 1e12})
+            rows.append({"workload": workload, "rep": r, "kernel": name,
+                         "TFLOP/s": 2.0 * M * N * K * launches / (ms * 1e-3) / 1e12})
     for p in plans.values():
         p.close()
     return rows
@@ -214,7 +229,8 @@ if __name__ == "__main__":
     elif what == "ablation":
         print(ablation(sys.argv[2] if len(sys.argv) > 2 else "c3"), flush=True)
     elif what == "library":
-        for row in library():
+        for row in library(sys.argv[2] if len(sys.argv) > 2 else "c3",
+                           launches=int(sys.argv[3]) if len(sys.argv) > 3 else 6):
             print(row, flush=True)
     elif what == "lds":
         lds()
