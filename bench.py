@@ -47,29 +47,83 @@ def load_traffic(workload: str, shape_index: int, kernel: str) -> float | None:
     return float(d["hbm_bytes_per_launch"])
 
 
-def cpu_baseline(a_bits, b_bits, K, in_dt, out_dt, seconds: float) -> dict:
-    """The oracle (fp64 triple loop) on the host cores, on a bounded row sample of the workload."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(a_bits, b_bits, K, in_dt, out_dt, c_gpu, seconds: float, full_seconds: float):
+    """The oracle (fp64 triple loop) on the host cores, over rows of the workload, timed; every row it
+    computes is also compared with the timed GPU result (c_gpu, the last launch's output bits).
+
+    All rows are computed when that is projected to take at most `full_seconds`, else the leading rows
+    that fit in about `seconds`. Returns (cpu_baseline object, parity object)."""
+    import numpy as np
+
     from oracle import oracle as orc
 
-    threads = max(1, min(16, os.cpu_count() or 1))
-    N = b_bits.shape[0]
+    threads = orc.cpu_share()
+    M, N = a_bits.shape[0], b_bits.shape[0]
+    block = max(threads, ((1 << 24) // max(N, 1)) // threads * threads)  # about 16 M outputs per call
+    parity = {"n_checked": 0, "of": M * N, "max_err_over_tol": 0.0, "n_fail": 0, "worst_index": None,
+              "rule": "|C - C_ref| <= 2e-3 (|A||B|^T)_ij + 1 ulp of the output type, every checked output"}
+    oracle_s = 0.0
 
-    def timed(rows: int) -> float:
+    def run(r0: int, r1: int) -> float:
         t0 = time.perf_counter()
-        orc.gemm(a_bits[:rows], b_bits, K, in_dt, out_dt, threads=threads, want_sums=False)
-        return time.perf_counter() - t0
+        c_ref, _, t = orc.gemm(a_bits[r0:r1], b_bits, K, in_dt, out_dt, threads=threads, want_s=False)
+        dt = time.perf_counter() - t0
+        rep = orc.compare(np.ascontiguousarray(c_gpu[r0:r1, :N]), c_ref, t, out_dt, rel=2e-3)
+        parity["n_checked"] += rep["n"]
+        parity["n_fail"] += rep["n_fail"]
+        if rep["n"] and rep["max_ratio"] >= parity["max_err_over_tol"]:
+            parity["max_err_over_tol"] = rep["max_ratio"]
+            parity["worst_index"] = [int(rep["worst_index"][0]) + r0, int(rep["worst_index"][1])]
+        return dt
 
-    # a call costs a fixed part (decoding B, starting threads) plus a part per row of A: fit both
-    # from two short calls, then size the sample to about `seconds`
-    r1, r2 = threads, 3 * threads
-    t1, t2 = timed(r1), timed(r2)
-    per_row = max((t2 - t1) / (r2 - r1), 1e-6)
-    rows2 = int(min(a_bits.shape[0], max(r2, (seconds - max(t1 - per_row * r1, 0.0)) / per_row)))
-    rows2 = max(threads, (rows2 // threads) * threads)
-    dt = timed(rows2)
-    return {"value": 2.0 * rows2 * N * K / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"rows 0..{rows2 - 1} of A against all {N} rows of B (K={K}); "
-                      f"{2.0 * rows2 * N * K:.3e} flop in {dt:.2f} s, fp64 triple loop, {threads} threads"}
+    # a call costs a fixed part (decoding B, starting threads) plus a part per row of A: two short
+    # calls fit both, then the sample is sized
+    r1 = min(M, threads)
+    r2 = min(M, r1 + 2 * threads)
+    t1 = run(0, r1)
+    t2 = run(r1, r2) if r2 > r1 else t1
+    oracle_s += t1 + t2
+    per_row = max((t2 - t1) / max(r2 - 2 * r1, 1), 1e-7) if r2 - r1 > r1 else max(t2 / max(r2 - r1, 1), 1e-7)
+    fixed = max(t1 - per_row * r1, 0.0)
+    rest = M - r2
+    full = fixed * (-(-rest // block)) + per_row * rest <= full_seconds
+    end = M if full else min(M, r2 + max(0, int((seconds - oracle_s) / per_row)))
+    done = r2
+    while done < end:
+        nxt = min(end, done + block)
+        oracle_s += run(done, nxt)
+        done = nxt
+    parity["ok"] = parity["n_fail"] == 0
+    flop = 2.0 * done * N * K
+    # one thread on the smallest workload (256^3, fp16 -> fp32)
+    import synthetic_inputs as si
+    _, _, k1, a1, b1, i1, o1 = si.workload_operands("c1_256_f16_f32")
+    t0 = time.perf_counter()
+    orc.gemm(a1, b1, k1, i1, o1, threads=1, want_sums=False)
+    st = time.perf_counter() - t0
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = None
+    base = {"value": flop / oracle_s / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": (f"rows 0..{done - 1} of A against all {N} rows of B (K={K}){' (all rows)' if done == M else ''}; "
+                       f"{flop:.3e} flop in {oracle_s:.2f} s, fp64 triple loop, {threads} threads"),
+            "nproc": os.cpu_count(), "affinity_cpus": affinity, "cpu_model": cpu_model(),
+            "threads_rule": "the CPUs this process may use, at most 16 (one GPU's share of a shared host)",
+            "single_thread_c1": {"seconds": st, "GFLOP/s": 2.0 * 256 ** 3 / st / 1e9,
+                                 "workload": "c1_256_f16_f32 (256^3, f16 -> f32), 1 thread"}}
+    return base, parity
 
 
 def main() -> int:
@@ -81,7 +135,10 @@ def main() -> int:
     ap.add_argument("--shape-index", type=int, default=0)
     ap.add_argument("--config", default=None, help="JSON kernel-config override (ablations)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
+                    help="oracle time for a row sample when the whole workload would take longer than --cpu-full-seconds")
+    ap.add_argument("--cpu-full-seconds", type=float, default=45.0,
+                    help="compute (and check) every row with the oracle when that is projected to take at most this")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also launch one 1 GiB copy kernel (reference for memory-traffic counters)")
     ap.add_argument("--no-probes", action="store_true", help="skip the MFMA-peak and HBM-copy probes")
@@ -187,6 +244,16 @@ def main() -> int:
         ce.record(stream)
         torch.cuda.synchronize()
         extra["copy_probe_GBps"] = 2 * nbytes / (cs.elapsed_time(ce) * 1e-3) / 1e9
+        # read-only stream over the same 1 GiB (four times the MALL): the HBM read ceiling
+        spt.gemm_probe_read(src.data_ptr(), nbytes, sp)
+        best = 0.0
+        for _ in range(3):
+            cs.record(stream)
+            spt.gemm_probe_read(src.data_ptr(), nbytes, sp)
+            ce.record(stream)
+            torch.cuda.synchronize()
+            best = max(best, nbytes / (cs.elapsed_time(ce) * 1e-3) / 1e9)
+        extra["hbm_read_probe_GBps"] = best
         del src, dst
 
     line = {
@@ -216,7 +283,10 @@ def main() -> int:
         "extra": extra,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(a_bits, b_bits, K, in_dt, out_dt, args.cpu_seconds)
+        # the output of the last timed launch, checked against the oracle rows the baseline computes
+        c_bits = C.cpu().numpy() if out_dt == 2 else C.cpu().view(torch.int16).numpy().view(np.uint16)
+        line["cpu_baseline"], line["parity"] = cpu_baseline(a_bits, b_bits, K, in_dt, out_dt, c_bits,
+                                                            args.cpu_seconds, args.cpu_full_seconds)
     plan.close()
     print(json.dumps(line), flush=True)
     return 0

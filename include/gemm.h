@@ -117,6 +117,7 @@ typedef struct gemm_plan_s* gemm_plan_t;
  *   c_dtype   GEMM_F16, GEMM_BF16 or GEMM_F32
  *   lda >= K, ldb >= K, ldc >= N   leading dimensions in elements
  *   config    NULL for the built-in choice, else an explicit configuration (validated)
+ * An override is validated (against 256 CUs and 160 KiB of LDS) before the device is queried.
  * Errors: GEMM_ERR_INVALID (null out, bad sizes or ld, invalid override),
  *         GEMM_ERR_UNSUPPORTED (dtype pair, a tile whose row span exceeds 2^31 bytes, an override
  *         whose workspace exceeds the caps: 1 GiB of partial planes, 3 GiB of staged operands,
@@ -173,14 +174,16 @@ const char* gemm_status_string(gemm_status_t status);
  * ---------------------------------------------------------------------------------------- */
 
 /*
- * The configuration gemm_plan_create would choose for this problem on a device with `cu_count`
- * compute units and `lds_bytes` of LDS per workgroup, assuming 16-byte aligned pointers.
- * Same argument checks and errors as gemm_plan_create (minus GEMM_ERR_HIP).
+ * The configuration gemm_plan_create would launch for this problem on a device with `cu_count`
+ * compute units and `lds_bytes` of LDS per workgroup, assuming 16-byte aligned pointers: the
+ * built-in choice when `config` is NULL, else the override after the same validation (so every
+ * override error can be checked without a GPU). Same argument checks and errors as
+ * gemm_plan_create (minus GEMM_ERR_HIP and GEMM_ERR_NOMEM).
  */
 gemm_status_t gemm_select_config(int64_t M, int64_t N, int64_t K, gemm_dtype_t a_dtype,
                                  gemm_dtype_t b_dtype, gemm_dtype_t c_dtype, int64_t lda,
                                  int64_t ldb, int64_t ldc, int cu_count, int lds_bytes,
-                                 gemm_config_t* out);
+                                 const gemm_config_t* config, gemm_config_t* out);
 
 /*
  * The cut gemm_plan_create would make without an override (see gemm_plan_parts), on a device with
@@ -241,51 +244,14 @@ gemm_status_t gemm_probe_copy(const void* src, void* dst, int64_t bytes, void* s
 gemm_status_t gemm_probe_lds_read(int swizzle, int64_t iters, void* stream);
 
 /*
- * Launch an LDS read-bandwidth kernel: one workgroup of 8 waves per CU, each wave keeping 16
- * independent ds_read_b128 (16 bytes per lane, consecutive addresses, conflict-free) in flight,
- * `iters` times. *bytes_read receives the bytes the launch reads from LDS.
- * Errors: GEMM_ERR_INVALID (iters < 1, null bytes_read), GEMM_ERR_HIP.
+ * Launch a read-only streaming kernel over `bytes` (a multiple of 16) at src: 16-byte loads, eight
+ * in flight per thread, nothing written but one word that no input selects. Over a buffer larger
+ * than the 256 MB MALL it measures the HBM read bandwidth, the ceiling of a memory-bound GEMM's
+ * operand stream ("Multi-Stage Software Pipelining", Performance: DRAM throughput is the figure
+ * the pages read for a load-bound loop). The caller times it with events.
+ * Errors: GEMM_ERR_INVALID (null src, bytes negative or not a multiple of 16), GEMM_ERR_HIP.
  */
-gemm_status_t gemm_probe_lds_bw(int64_t iters, void* stream, double* bytes_read);
-
-/*
- * Launch a global->LDS fill kernel (the staging path of the GEMM's mainloop): one workgroup of
- * 4 waves per CU; per iteration every wave issues 16 direct 1 KiB loads (buffer_load_dwordx4 ...
- * lds), two iterations in flight. Workgroup w reads the `region` bytes of src at w*region,
- * wrapping inside them; when region times the CU count exceeds `bytes`, every workgroup reads the
- * first `region` bytes instead. A small region keeps the reads L2-resident, a large one streams.
- * *bytes_moved receives the bytes the launch loads into LDS.
- * Errors: GEMM_ERR_INVALID (null pointer, iters < 1, bytes outside [64 KiB, 2^31 - 64 KiB], region
- * not a multiple of 64 KiB or larger than bytes), GEMM_ERR_HIP.
- */
-gemm_status_t gemm_probe_fill(const void* src, int64_t bytes, int64_t region, int64_t iters, void* stream,
-                              double* bytes_moved);
-
-/*
- * Launch a global->LDS issue-rate kernel: one workgroup of 16 waves per CU, of which the first
- * `waves` (1..16) issue direct 1 KiB loads (buffer_load_dwordx4 ... lds) from the CU's own 64 KiB
- * of src (so the reads hit L2), each wave keeping `depth` (1, 2, 4, 8 or 16) loads in flight;
- * iters x 8 loads per issuing wave. Measures how fast one wave, and one CU, can stage operand tiles.
- * *bytes_moved receives the bytes the launch loads into LDS.
- * Errors: GEMM_ERR_INVALID (null pointer, iters < 1, waves outside 1..16, depth not a listed value,
- * bytes below 64 KiB per CU or above 2^31 - 64 KiB), GEMM_ERR_HIP.
- */
-gemm_status_t gemm_probe_dma_rate(const void* src, int64_t bytes, int waves, int depth, int64_t iters, void* stream,
-                                  double* bytes_moved);
-
-/*
- * Launch a store-pattern kernel: one workgroup of 8 waves per CU; the workgroups w with
- * w / 8 < active_per_xcd (that many per XCD) each write a 256-row x 512-byte block of dst at
- * w*256*ldc, iters times, with 16-byte stores. Every store instruction covers rows_per_instr
- * (2, 4, 8 or 16) rows of 1024/rows_per_instr bytes; layout 0 gives lane l row l mod
- * rows_per_instr (the order in which an MFMA hands out rows), layout 1 puts consecutive lanes
- * along a row. Measures how the row shape of an epilogue's stores sets its speed.
- * *bytes_written receives the bytes the launch writes. dst must hold CU count x 256 x ldc bytes.
- * Errors: GEMM_ERR_INVALID (null pointer, a value outside the lists, iters < 1, active_per_xcd < 1,
- * ldc < 512 or not a multiple of 16, 256*ldc above 2^31 - 64 KiB, bytes too small), GEMM_ERR_HIP.
- */
-gemm_status_t gemm_probe_store(void* dst, int64_t bytes, int64_t ldc, int rows_per_instr, int layout,
-                               int active_per_xcd, int64_t iters, void* stream, double* bytes_written);
+gemm_status_t gemm_probe_read(const void* src, int64_t bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -97,19 +97,30 @@ def _check_operands(a_bits, b_bits, K):
     return a, b
 
 
+def cpu_share() -> int:
+    """Threads the oracle runs on by default: the CPUs this process may use, at most 16 (the
+    host-core share of one GPU on a shared GPU host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
 def gemm(a_bits: np.ndarray, b_bits: np.ndarray, K: int, in_dtype: int, out_dtype: int,
-         threads: int | None = None, want_sums: bool = True):
+         threads: int | None = None, want_sums: bool = True, want_s: bool = True):
     """Full product C = A·Bᵀ over the first K columns of A[M, lda] and B[N, ldb].
 
     Returns (C_ref, S, T): C_ref as uint16 bits or float32, dense [M, N]; S and T the float64
-    sums (None unless ``want_sums``).
+    sums (None unless ``want_sums``; S also None when ``want_s`` is false, for callers that
+    only need the tolerance scale T).
     """
     a, b = _check_operands(a_bits, b_bits, K)
     M, N = a.shape[0], b.shape[0]
     c = np.empty((M, N), dtype=np.float32 if out_dtype == F32 else np.uint16)
-    s = np.empty((M, N), dtype=np.float64) if want_sums else None
+    s = np.empty((M, N), dtype=np.float64) if want_sums and want_s else None
     t = np.empty((M, N), dtype=np.float64) if want_sums else None
-    threads = threads or min(os.cpu_count() or 1, 16)
+    threads = threads or cpu_share()
     rc = lib().oracle_gemm(M, N, K, in_dtype, _ptr(a), a.shape[1], _ptr(b), b.shape[1], out_dtype,
                            _ptr(c), N, _ptr(s) if s is not None else None,
                            _ptr(t) if t is not None else None, threads)

@@ -20,7 +20,7 @@ GEMM_LOAD_AUTO, GEMM_LOAD_DMA, GEMM_LOAD_REG, GEMM_LOAD_STAGED = 0, 1, 2, 3
 EXPORTS = ("gemm_plan_create", "gemm_run", "gemm_plan_destroy", "gemm_plan_describe", "gemm_plan_workspace_bytes",
            "gemm_plan_parts", "gemm_status_string",
            "gemm_select_config", "gemm_select_parts", "gemm_schedule_tile", "gemm_lds_chunk_offset", "gemm_probe_mfma_peak",
-           "gemm_probe_copy", "gemm_probe_lds_read", "gemm_probe_lds_bw", "gemm_probe_fill", "gemm_probe_dma_rate", "gemm_probe_store")
+           "gemm_probe_copy", "gemm_probe_read", "gemm_probe_lds_read")
 
 
 class GemmLibraryMissing(ImportError):
@@ -79,7 +79,8 @@ def lib() -> ctypes.CDLL:
     L.gemm_status_string.restype = ctypes.c_char_p
     L.gemm_status_string.argtypes = [i32]
     L.gemm_select_config.restype = i32
-    L.gemm_select_config.argtypes = [i64, i64, i64, i32, i32, i32, i64, i64, i64, i32, i32, P(GemmConfig)]
+    L.gemm_select_config.argtypes = [i64, i64, i64, i32, i32, i32, i64, i64, i64, i32, i32, P(GemmConfig),
+                                     P(GemmConfig)]
     L.gemm_schedule_tile.restype = i32
     L.gemm_schedule_tile.argtypes = [i64, i64, i32, i32, i32, i32, i32, P(i64), P(i64), P(i32)]
     L.gemm_lds_chunk_offset.restype = i64
@@ -90,14 +91,8 @@ def lib() -> ctypes.CDLL:
     L.gemm_probe_copy.argtypes = [vp, vp, i64, vp]
     L.gemm_probe_lds_read.restype = i32
     L.gemm_probe_lds_read.argtypes = [i32, i64, vp]
-    L.gemm_probe_lds_bw.restype = i32
-    L.gemm_probe_lds_bw.argtypes = [i64, vp, P(ctypes.c_double)]
-    L.gemm_probe_fill.restype = i32
-    L.gemm_probe_fill.argtypes = [vp, i64, i64, i64, vp, P(ctypes.c_double)]
-    L.gemm_probe_dma_rate.restype = i32
-    L.gemm_probe_dma_rate.argtypes = [vp, i64, i32, i32, i64, vp, P(ctypes.c_double)]
-    L.gemm_probe_store.restype = i32
-    L.gemm_probe_store.argtypes = [vp, i64, i64, i32, i32, i32, i64, vp, P(ctypes.c_double)]
+    L.gemm_probe_read.restype = i32
+    L.gemm_probe_read.argtypes = [vp, i64, vp]
     _lib = L
     return L
 
@@ -166,18 +161,27 @@ def gemm_plan_workspace_bytes(plan: int) -> int:
     return n.value
 
 
-def gemm_select_config(M, N, K, a_dtype, b_dtype, c_dtype, lda, ldb, ldc, cu_count=256, lds_bytes=160 * 1024) -> dict:
+def _config_ref(config):
+    if config is None:
+        return None
+    if isinstance(config, dict):
+        config = GemmConfig.from_dict(config)
+    return ctypes.byref(config)
+
+
+def gemm_select_config(M, N, K, a_dtype, b_dtype, c_dtype, lda, ldb, ldc, cu_count=256, lds_bytes=160 * 1024,
+                       config=None) -> dict:
     c = GemmConfig()
     _check(lib().gemm_select_config(M, N, K, a_dtype, b_dtype, c_dtype, lda, ldb, ldc, cu_count, lds_bytes,
-                                    ctypes.byref(c)), "gemm_select_config")
+                                    _config_ref(config), ctypes.byref(c)), "gemm_select_config")
     return c.as_dict()
 
 
 def gemm_select_config_status(M, N, K, a_dtype, b_dtype, c_dtype, lda, ldb, ldc, cu_count=256,
-                              lds_bytes=160 * 1024) -> int:
+                              lds_bytes=160 * 1024, config=None) -> int:
     c = GemmConfig()
     return lib().gemm_select_config(M, N, K, a_dtype, b_dtype, c_dtype, lda, ldb, ldc, cu_count, lds_bytes,
-                                    ctypes.byref(c))
+                                    _config_ref(config), ctypes.byref(c))
 
 
 def gemm_schedule_tile(tiles_m, tiles_n, splits, group_m, grid, wg, rnd):
@@ -209,29 +213,5 @@ def gemm_probe_lds_read(swizzle: int, iters: int, stream: int = 0) -> None:
     _check(lib().gemm_probe_lds_read(swizzle, iters, stream or None), "gemm_probe_lds_read")
 
 
-def gemm_probe_fill(src_ptr: int, nbytes: int, region: int, iters: int, stream: int = 0) -> float:
-    moved = ctypes.c_double()
-    _check(lib().gemm_probe_fill(src_ptr, nbytes, region, iters, stream or None, ctypes.byref(moved)),
-           "gemm_probe_fill")
-    return moved.value
-
-
-def gemm_probe_dma_rate(src_ptr: int, nbytes: int, waves: int, depth: int, iters: int, stream: int = 0) -> float:
-    moved = ctypes.c_double()
-    _check(lib().gemm_probe_dma_rate(src_ptr, nbytes, waves, depth, iters, stream or None, ctypes.byref(moved)),
-           "gemm_probe_dma_rate")
-    return moved.value
-
-
-def gemm_probe_store(dst_ptr: int, nbytes: int, ldc: int, rows_per_instr: int, layout: int, active_per_xcd: int,
-                     iters: int, stream: int = 0) -> float:
-    written = ctypes.c_double()
-    _check(lib().gemm_probe_store(dst_ptr, nbytes, ldc, rows_per_instr, layout, active_per_xcd, iters,
-                                  stream or None, ctypes.byref(written)), "gemm_probe_store")
-    return written.value
-
-
-def gemm_probe_lds_bw(iters: int, stream: int = 0) -> float:
-    nbytes = ctypes.c_double()
-    _check(lib().gemm_probe_lds_bw(iters, stream or None, ctypes.byref(nbytes)), "gemm_probe_lds_bw")
-    return nbytes.value
+def gemm_probe_read(src_ptr: int, nbytes: int, stream: int = 0) -> None:
+    _check(lib().gemm_probe_read(src_ptr, nbytes, stream or None), "gemm_probe_read")

@@ -40,6 +40,7 @@ struct gemm_plan_s {
 namespace {
 
 constexpr int kMaxLds = 160 * 1024;
+constexpr int kGfx950Cus = 256;  // MI355X
 constexpr int kMaxSplits = 16;
 constexpr int kMinKtPerSplit = 8;                           // K-tiles a split-K unit keeps at least
 constexpr int64_t kMaxPartialBytes = (int64_t)1 << 30;      // fp32 partial planes of a split-K plan
@@ -397,9 +398,9 @@ const char* gemm_status_string(gemm_status_t s) {
 
 gemm_status_t gemm_select_config(int64_t M, int64_t N, int64_t K, gemm_dtype_t a_dtype, gemm_dtype_t b_dtype,
                                  gemm_dtype_t c_dtype, int64_t lda, int64_t ldb, int64_t ldc, int cu_count,
-                                 int lds_bytes, gemm_config_t* out) {
+                                 int lds_bytes, const gemm_config_t* config, gemm_config_t* out) {
   if (!out) return GEMM_ERR_INVALID;
-  return select_impl(M, N, K, a_dtype, b_dtype, c_dtype, lda, ldb, ldc, cu_count, lds_bytes, nullptr, out, nullptr);
+  return select_impl(M, N, K, a_dtype, b_dtype, c_dtype, lda, ldb, ldc, cu_count, lds_bytes, config, out, nullptr);
 }
 
 gemm_status_t gemm_plan_create(gemm_plan_t* out, int64_t M, int64_t N, int64_t K, gemm_dtype_t a_dtype,
@@ -409,6 +410,14 @@ gemm_status_t gemm_plan_create(gemm_plan_t* out, int64_t M, int64_t N, int64_t K
   *out = nullptr;
   gemm_status_t st = check_args(M, N, K, a_dtype, b_dtype, c_dtype, lda, ldb, ldc);
   if (st != GEMM_OK) return st;
+  if (config) {
+    // An override is validated before the device query, against the CU count and LDS of the
+    // device the kernels are built for, so a bad configuration reports its own status on any host.
+    gemm_config_t checked;
+    st = select_impl(M, N, K, a_dtype, b_dtype, c_dtype, lda, ldb, ldc, kGfx950Cus, kMaxLds, config, &checked,
+                     nullptr);
+    if (st != GEMM_OK) return st;
+  }
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return GEMM_ERR_HIP;
   hipDeviceProp_t prop;

@@ -97,8 +97,10 @@ __global__ void __launch_bounds__(WM* WN * 64, 1) gemm_dma_kernel(GemmArgs args)
       if (args.queue == nullptr) return t + args.grid;
       int* const slot = (int*)(smem + T::LDS);
       if (threadIdx.x == 0) *slot = args.grid + atomicAdd(&args.queue[0], 1);
+      wait_lgkmcnt0();  // the slot write has reached LDS before any wave passes the barrier
       barrier_sync();
       const int n = *slot;
+      wait_lgkmcnt0();  // every wave's read of the slot is done before the next take may overwrite it
       barrier_sync();
       return n;
     }

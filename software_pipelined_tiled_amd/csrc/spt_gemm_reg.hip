@@ -8,6 +8,10 @@
 // element and zero-filled past K. Two LDS stages: tile k+1 is written from registers at the
 // end of tile k, and tile k+2's global loads are issued right after the hand-over barrier, so
 // they are in flight while tile k+1 is computed. One barrier per K-tile.
+// One stage (S = 1) is the synchronous relay of "GEMM II — pipelining with TMA" (Forced move:
+// every thread loads, writes the tile and waits, then the tile is computed): per K-tile the global
+// loads, the LDS writes, a barrier, the MFMAs, and a second barrier before the slot is rewritten.
+// It is kept as the first rung of the stage-count ablation.
 #include "spt_device.h"
 #include "spt_kernels.h"
 
@@ -30,9 +34,9 @@ __device__ __forceinline__ u32x4 load_chunk(__amdgpu_buffer_rsrc_t r, bool row_o
   return v;
 }
 
-template <int BM, int BN, int BK, int WM, int WN, typename TIn, int OUT>
+template <int BM, int BN, int BK, int S, int WM, int WN, typename TIn, int OUT>
 __global__ void __launch_bounds__(WM* WN * 64, 1) gemm_reg_kernel(GemmArgs args) {
-  constexpr int S = 2;
+  static_assert(S == 1 || S == 2, "one stage (serial) or two");
   using T = TileShape<BM, BN, BK, S, WM, WN>;
   constexpr int CPR = BK / 8;                          // chunks per row
   constexpr int CA = BM * CPR / T::NT, CB = BN * CPR / T::NT;  // chunks per thread per stage
@@ -145,14 +149,42 @@ __global__ void __launch_bounds__(WM* WN * 64, 1) gemm_reg_kernel(GemmArgs args)
       barrier_sync();
     }
     first_tile = false;
-    gload(0);
-    lstore(0);
-    wait_lgkmcnt0();
-    barrier_sync();
-    if (KT > 1) gload(1);
-    read_frags(0, 0, 0);
-    k_tile(0, 0, std::true_type{});
-    for (int k = 1; k < KT; ++k) k_tile(k, k & 1, std::false_type{});
+    if constexpr (S == 1) {
+      // the synchronous relay: load, write, wait, compute, then free the slot for the next K-tile
+      auto serial_tile = [&](int k, auto first_c) {
+        constexpr bool kFirst = decltype(first_c)::value;
+        if (k > 0) {
+          wait_lgkmcnt0();  // this wave's reads of the slot are done
+          barrier_sync();   // ... and every other wave's
+        }
+        gload(k);
+        lstore(0);
+        wait_lgkmcnt0();
+        barrier_sync();  // the tile is in LDS for every wave
+        read_frags(0, 0, 0);
+#pragma unroll
+        for (int sub = 0; sub < T::NSUB; ++sub) {
+          const int buf = sub & 1;
+          if (sub + 1 < T::NSUB) read_frags(0, sub + 1, buf ^ 1);
+#pragma unroll
+          for (int i = 0; i < T::FN; ++i)
+#pragma unroll
+            for (int j = 0; j < T::FM; ++j)
+              acc[i][j] = mfma16<TIn>(xf[buf][i], yf[buf][j], (kFirst && sub == 0) ? zero4 : acc[i][j]);
+        }
+      };
+      serial_tile(0, std::true_type{});
+      for (int k = 1; k < KT; ++k) serial_tile(k, std::false_type{});
+    } else {
+      gload(0);
+      lstore(0);
+      wait_lgkmcnt0();
+      barrier_sync();
+      if (KT > 1) gload(1);
+      read_frags(0, 0, 0);
+      k_tile(0, 0, std::true_type{});
+      for (int k = 1; k < KT; ++k) k_tile(k, k & 1, std::false_type{});
+    }
 
     auto epilogue = [&](auto edge_c) {
       constexpr bool kEdge = decltype(edge_c)::value;
@@ -176,26 +208,27 @@ __global__ void __launch_bounds__(WM* WN * 64, 1) gemm_reg_kernel(GemmArgs args)
   }
 }
 
-template <int BM, int BN, int BK, int WM, int WN>
+template <int BM, int BN, int BK, int S, int WM, int WN>
 static KernelEntry make_reg_entry() {
-  using T = TileShape<BM, BN, BK, 2, WM, WN>;
+  using T = TileShape<BM, BN, BK, S, WM, WN>;
   KernelEntry e;
-  e.bm = BM; e.bn = BN; e.bk = BK; e.stages = 2; e.waves = T::W; e.load_path = 2;
+  e.bm = BM; e.bn = BN; e.bk = BK; e.stages = S; e.waves = T::W; e.load_path = 2;
   e.lds_bytes = T::LDS;
   e.mfma = 16;
-  e.fn[0][0] = (const void*)&gemm_reg_kernel<BM, BN, BK, WM, WN, _Float16, 0>;
-  e.fn[0][1] = (const void*)&gemm_reg_kernel<BM, BN, BK, WM, WN, _Float16, 1>;
-  e.fn[0][2] = (const void*)&gemm_reg_kernel<BM, BN, BK, WM, WN, _Float16, 2>;
-  e.fn[1][0] = (const void*)&gemm_reg_kernel<BM, BN, BK, WM, WN, __bf16, 0>;
-  e.fn[1][1] = (const void*)&gemm_reg_kernel<BM, BN, BK, WM, WN, __bf16, 1>;
-  e.fn[1][2] = (const void*)&gemm_reg_kernel<BM, BN, BK, WM, WN, __bf16, 2>;
+  e.fn[0][0] = (const void*)&gemm_reg_kernel<BM, BN, BK, S, WM, WN, _Float16, 0>;
+  e.fn[0][1] = (const void*)&gemm_reg_kernel<BM, BN, BK, S, WM, WN, _Float16, 1>;
+  e.fn[0][2] = (const void*)&gemm_reg_kernel<BM, BN, BK, S, WM, WN, _Float16, 2>;
+  e.fn[1][0] = (const void*)&gemm_reg_kernel<BM, BN, BK, S, WM, WN, __bf16, 0>;
+  e.fn[1][1] = (const void*)&gemm_reg_kernel<BM, BN, BK, S, WM, WN, __bf16, 1>;
+  e.fn[1][2] = (const void*)&gemm_reg_kernel<BM, BN, BK, S, WM, WN, __bf16, 2>;
   return e;
 }
 
 const KernelEntry* reg_kernel_table(int* count) {
   static const KernelEntry table[] = {
-      make_reg_entry<128, 128, 64, 2, 2>(),
-      make_reg_entry<64, 64, 64, 2, 2>(),
+      make_reg_entry<128, 128, 64, 2, 2, 2>(),
+      make_reg_entry<64, 64, 64, 2, 2, 2>(),
+      make_reg_entry<128, 128, 64, 1, 2, 2>(),  // the serial rung of the stage-count ablation
   };
   *count = (int)(sizeof(table) / sizeof(table[0]));
   return table;

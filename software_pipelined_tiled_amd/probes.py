@@ -1,25 +1,16 @@
 """Measurement probes, run as ``python -m software_pipelined_tiled_amd.probes <what>``:
 
-    peak    dense MFMA throughput (16x16x32 bf16) in TFLOP/s, 1 and 2 waves per SIMD
-    copy    16-byte streaming copy bandwidth in GB/s (read + write)
-    lds     the LDS read-pattern kernels, one launch per swizzle (read the counters with rocprofv3)
-    fill    global->LDS fill rate per CU: each workgroup re-reading its own 64 KiB (L2-resident),
-            and streaming 4 MiB of its own (L2 misses)
-    dma     global->LDS issue rate: 1, 4, 8 or 16 issuing waves per CU, each keeping 1..16 loads in
-            flight, L2-resident reads
-    ldsbw   LDS read bandwidth per CU: 8 waves per CU, 16 independent ds_read_b128 per wave in flight
-    store   epilogue store shapes: rows per store instruction (16, 8, 4, 2) x lane layout, with 1, 8
-            or 32 writing workgroups per XCD
+    peak     dense MFMA throughput (16x16x32 bf16) in TFLOP/s, 1 and 2 waves per SIMD
+    copy     16-byte streaming copy bandwidth in GB/s (read + write)
+    read     16-byte read-only stream over 1 GiB (more than the 256 MB MALL), in GB/s: the HBM read
+             ceiling of a memory-bound GEMM's operand stream
+    lds      the LDS read-pattern kernels, one launch per swizzle (read the counters with rocprofv3)
     ablation [c3|c4] the stage-count ablation: every tile and ring depth of the menu, persistent (static
-            rounds or the dynamic queue) and not, group_m 1 and the 32x32x16 MFMA form, each forced
-            through the configuration override;
-            one untimed pass, then two alternating passes of 10 launches; prints a markdown table of
-            TFLOP/s
-    library [c3|c4|c2|c5a|c5b|c5c [launches]] one workload (8192^3 bf16 by default, inputs drawn with
-            torch in the workload's distribution) through this library's default plan (for 8192^3
-            also its 4-wave 256x256 split-ring plan) and, for context only, torch.mm (the vendor GEMM
-            library), in alternating blocks of launches; prints TFLOP/s per block. Run it under
-            rocprofv3 --pmc to compare clock, MFMA utilisation and instruction mix per kernel.
+             rounds or the dynamic queue) and not, group_m 1 and the 32x32x16 MFMA form, each forced
+             through the configuration override; one untimed pass, then two alternating passes of 10
+             launches; prints a markdown table of TFLOP/s, then the pipeline Gantt model's prediction
+             for each tile's ring depths, fed with the measured serial (S = 1) K-tile time and the MFMA
+             peak measured in the same process
 """
 from __future__ import annotations
 
@@ -28,9 +19,10 @@ import sys
 import torch
 
 from . import _lib
+from . import gantt
 
 
-def _timed(fn) -> float:
+def _timed(fn):
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s.record()
     out = fn()
@@ -56,97 +48,15 @@ def copy(nbytes: int = 1 << 30) -> float:
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
-def fill(iters: int = 2000) -> dict:
-    nbytes = 1 << 30
+def read(nbytes: int = 1 << 30, reps: int = 5) -> float:
+    """Best of `reps` timed read streams over `nbytes` (after one untimed pass), in GB/s."""
     src = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
-    cus = torch.cuda.get_device_properties(0).multi_processor_count
-    res = {}
-    for name, region in (("l2_resident_64KiB_per_cu", 1 << 16), ("streaming_4MiB_per_cu", 1 << 22)):
-        _lib.gemm_probe_fill(src.data_ptr(), nbytes, region, 8)
-        ms, moved = _timed(lambda: _lib.gemm_probe_fill(src.data_ptr(), nbytes, region, iters))
-        res[name + "_GBps_total"] = moved / (ms * 1e-3) / 1e9
-        res[name + "_B_per_ns_per_cu"] = moved / (ms * 1e6) / cus
-    return res
-
-
-def dma(iters: int = 1000) -> list[dict]:
-    cus = torch.cuda.get_device_properties(0).multi_processor_count
-    nbytes = cus * 65536
-    src = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
-    rows = []
-    for waves in (1, 4, 8, 16):
-        for depth in (1, 2, 4, 8, 16):
-            _lib.gemm_probe_dma_rate(src.data_ptr(), nbytes, waves, depth, 4)
-            ms, moved = _timed(lambda: _lib.gemm_probe_dma_rate(src.data_ptr(), nbytes, waves, depth, iters))
-            per_cu = moved / (ms * 1e6) / cus
-            rows.append({"waves": waves, "depth": depth, "B_per_ns_per_cu": per_cu,
-                         "B_per_ns_per_wave": per_cu / waves, "ns_per_load_per_wave": 1024.0 / (per_cu / waves)})
-    return rows
-
-
-def store(iters: int = 20, ldc: int = 32768) -> list[dict]:
-    cus = torch.cuda.get_device_properties(0).multi_processor_count
-    nbytes = cus * 256 * ldc
-    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
-    rows = []
-    for r, layout in ((16, 0), (16, 1), (8, 1), (4, 1), (2, 1)):
-        for active in (1, 8, 32):
-            _lib.gemm_probe_store(dst.data_ptr(), nbytes, ldc, r, layout, active, 2)
-            ms, written = _timed(lambda: _lib.gemm_probe_store(dst.data_ptr(), nbytes, ldc, r, layout, active, iters))
-            wgs = min(active * 8, cus)
-            rows.append({"rows_per_instr": r, "layout": "mfma rows" if layout == 0 else "along a row",
-                         "active_per_xcd": active, "us_per_128KiB": ms * 1e3 / iters,
-                         "GB_per_s_per_cu": written / wgs / (ms * 1e-3) / 1e9,
-                         "GB_per_s_total": written / (ms * 1e-3) / 1e9})
-    return rows
-
-
-def ldsbw(iters: int = 4000) -> dict:
-    cus = torch.cuda.get_device_properties(0).multi_processor_count
-    _lib.gemm_probe_lds_bw(10)
-    ms, nbytes = _timed(lambda: _lib.gemm_probe_lds_bw(iters))
-    per_cu = nbytes / (ms * 1e6) / cus
-    return {"B_per_ns_per_cu": per_cu, "B_per_clk_per_cu_if_2.4GHz": per_cu / 2.4,
-            "TB_per_s_total": nbytes / (ms * 1e-3) / 1e12}
-
-
-LIBRARY_SHAPES = {"c3": (8192, 8192, 8192, torch.bfloat16, "normal"),
-                  "c4": (16384, 16384, 1024, torch.bfloat16, "uniform"),
-                  "c2": (4096, 4096, 4096, torch.float16, "uniform"),
-                  "c5a": (32, 8192, 8192, torch.float16, "uniform"),
-                  "c5b": (4093, 5119, 3071, torch.float16, "uniform"),
-                  "c5c": (8192, 1024, 28672, torch.float16, "uniform")}
-
-
-def library(workload: str = "c3", reps: int = 3, launches: int = 6) -> list[dict]:
-    from .torch_api import Plan
-
-    M, N, K, dt, dist = LIBRARY_SHAPES[workload]
-    g = torch.Generator(device="cuda").manual_seed(0)
-    if dist == "normal":
-        A = (torch.randn(M, K, device="cuda", generator=g) / K ** 0.5).to(dt)
-        B = (torch.randn(N, K, device="cuda", generator=g) / K ** 0.5).to(dt)
-    else:
-        A = (torch.rand(M, K, device="cuda", generator=g) * 2 - 1).to(dt)
-        B = (torch.rand(N, K, device="cuda", generator=g) * 2 - 1).to(dt)
-    C = torch.empty(M, N, dtype=dt, device="cuda")
-    plans = {"default plan": Plan(M, N, K, dt, dt)}
-    if workload == "c3":
-        four_wave = dict(bm=256, bn=256, bk=64, stages=5, waves=4, mfma=16, persistent=1, group_m=8, load_path=1,
-                         grid=0, lds_bytes=0, splits=1)
-        plans["4-wave split ring"] = Plan(M, N, K, dt, dt, config=four_wave)
-    sp = torch.cuda.current_stream().cuda_stream
-    runs = {name: (lambda p=p: p.run_ptrs(A.data_ptr(), B.data_ptr(), C.data_ptr(), sp)) for name, p in plans.items()}
-    runs["torch.mm (context)"] = lambda: torch.mm(A, B.t(), out=C)
-    rows = []
-    for r in range(reps):
-        for name, fn in runs.items():
-            ms, _ = _timed(lambda: [fn() for _ in range(launches)])
-            rows.append({"workload": workload, "rep": r, "kernel": name,
-                         "TFLOP/s": 2.0 * M * N * K * launches / (ms * 1e-3) / 1e12})
-    for p in plans.values():
-        p.close()
-    return rows
+    _lib.gemm_probe_read(src.data_ptr(), nbytes)
+    best = 0.0
+    for _ in range(reps):
+        ms, _ = _timed(lambda: _lib.gemm_probe_read(src.data_ptr(), nbytes))
+        best = max(best, nbytes / (ms * 1e-3) / 1e9)
+    return best
 
 
 ABLATION_SHAPES = {"c3": (8192, 8192, 8192, torch.bfloat16, "normal"),
@@ -164,12 +74,11 @@ ABLATION_ROWS = (
     + [("128x128", c, 128, 128, s, 4, 64, 1, p, 8, 16) for c, s, p in
        (("S=1 (serial)", 1, 1), ("S=2", 2, 1), ("S=3", 3, 1), ("S=4", 4, 1), ("non-persistent, S=4", 4, 0),
         ("dynamic queue, S=4", 4, 2))]
-    + [("128x128 register-staged", "S=2", 128, 128, 2, 4, 64, 2, 1, 8, 16)])
+    + [("128x128 register-staged", c, 128, 128, s, 4, 64, 2, 1, 8, 16) for c, s in
+       (("S=1 (serial)", 1), ("S=2", 2))])
 
 
-def ablation(workload: str = "c3", passes: int = 2, launches: int = 10) -> str:
-    from .torch_api import Plan
-
+def _operands(workload: str):
     M, N, K, dt, dist = ABLATION_SHAPES[workload]
     g = torch.Generator(device="cuda").manual_seed(0)
     if dist == "normal":
@@ -178,6 +87,44 @@ def ablation(workload: str = "c3", passes: int = 2, launches: int = 10) -> str:
     else:
         A = (torch.rand(M, K, device="cuda", generator=g) * 2 - 1).to(dt)
         B = (torch.rand(N, K, device="cuda", generator=g) * 2 - 1).to(dt)
+    return M, N, K, dt, A, B
+
+
+def gantt_table(workload: str, res: dict, peak_tflops: float, cus: int = 256) -> str:
+    """The Gantt model beside the measured ring depths of each 4-wave DMA tile: the MMA time of a
+    K-tile at the measured MFMA peak, the load time as the serial K-tile time less that, and the
+    model's TFLOP/s for every depth measured with a static persistent grid."""
+    M, N, K, _, _ = ABLATION_SHAPES[workload]
+    flop = 2.0 * M * N * K
+    out = [f"| {workload}: tile | K-tiles per tile, rounds | MMA / load per K-tile (us) | depth | measured TFLOP/s "
+           "| model TFLOP/s | model idle |", "|---|---|---|---|---|---|---|"]
+    for tile, bm, bn in (("256x256 4-wave", 256, 256), ("256x128", 256, 128), ("128x128", 128, 128)):
+        serial = res.get((tile, "S=1 (serial)"))
+        if not serial:
+            continue
+        kt = -(-K // 64)
+        tiles = -(-M // bm) * -(-N // bn)
+        rounds = -(-tiles // min(tiles, cus))
+        t1 = flop / (max(serial) * 1e12)                      # fastest serial launch, seconds
+        mma = 2.0 * bm * bn * 64 / (peak_tflops * 1e12 / cus)  # one K-tile at the measured MFMA peak
+        load = max(t1 / (rounds * kt) - mma, 0.0)
+        for col, vals in sorted((c, v) for (r, c), v in res.items() if r == tile):
+            if not col.startswith("S="):
+                continue
+            depth = int(col.split("=")[1].split()[0])
+            if depth > 4:
+                continue
+            t = gantt.predict_rounds(kt, depth, load, mma, rounds)
+            idle = gantt.simulate(kt, depth, load, mma, "serial" if depth == 1 else "prefetch")["idle"]
+            out.append(f"| {tile} | {kt}, {rounds} | {mma * 1e6:.3f} / {load * 1e6:.3f} | {depth} | "
+                       f"{' / '.join(f'{x:.0f}' for x in vals)} | {flop / t / 1e12:.0f} | {idle:.2f} |")
+    return "\n".join(out)
+
+
+def ablation(workload: str = "c3", passes: int = 2, launches: int = 10) -> str:
+    from .torch_api import Plan
+
+    M, N, K, dt, A, B = _operands(workload)
     C = torch.empty(M, N, dtype=dt, device="cuda")
     sp = torch.cuda.current_stream().cuda_stream
     plans = []
@@ -198,9 +145,12 @@ def ablation(workload: str = "c3", passes: int = 2, launches: int = 10) -> str:
             res[(r, c)].append(2.0 * M * N * K * launches / (ms * 1e-3) / 1e12)
     for _, _, p in plans:
         p.close()
+    pk = max(peak().values())
     out = [f"| {workload}: configuration | TFLOP/s (one per pass) |", "|---|---|"]
     for (r, c), v in res.items():
         out.append(f"| {r}, {c} | " + " / ".join(f"{x:.0f}" for x in v) + " |")
+    out += ["", f"MFMA peak probe, same process: {pk:.0f} TFLOP/s (best of one and two waves per SIMD)", "",
+            gantt_table(workload, res, pk)]
     return "\n".join(out)
 
 
@@ -216,22 +166,10 @@ if __name__ == "__main__":
         print(peak())
     elif what == "copy":
         print(f"{copy():.1f} GB/s")
-    elif what == "fill":
-        print(fill())
-    elif what == "dma":
-        for row in dma():
-            print(row)
-    elif what == "store":
-        for row in store():
-            print(row)
-    elif what == "ldsbw":
-        print(ldsbw())
+    elif what == "read":
+        print(f"{read():.1f} GB/s")
     elif what == "ablation":
         print(ablation(sys.argv[2] if len(sys.argv) > 2 else "c3"), flush=True)
-    elif what == "library":
-        for row in library(sys.argv[2] if len(sys.argv) > 2 else "c3",
-                           launches=int(sys.argv[3]) if len(sys.argv) > 3 else 6):
-            print(row, flush=True)
     elif what == "lds":
         lds()
         print("lds probes launched: swizzles -1, 0, 1, 2, 3, 4 in this order")

@@ -179,23 +179,60 @@ def test_split_choice_small_k_and_limits():
     assert c["splits"] * 2048 * 2048 * 4 <= 1 << 30
 
 
-def test_config_override_validation():
-    good = dict(bm=128, bn=128, bk=64, stages=4, waves=4, mfma=16, persistent=1, group_m=8, load_path=1, grid=0,
-                lds_bytes=0)
-    lib = spt.lib()
-    # not in the kernel table
-    bad = dict(good, bm=96)
+GOOD_OVERRIDE = dict(bm=128, bn=128, bk=64, stages=4, waves=4, mfma=16, persistent=1, group_m=8, load_path=1,
+                     grid=0, lds_bytes=0, splits=1)
+
+
+@pytest.mark.parametrize("shape,change,status", [
+    ((256, 256, 256), dict(bm=96), INVALID),                                  # no such kernel
+    ((256, 256, 256), dict(stages=5), INVALID),                               # no 128x128 split ring
+    ((256, 256, 256), dict(mfma=32), INVALID),                                # 32x32x16 only in the two-group kernel
+    ((256, 256, 256), dict(mfma=8), INVALID),
+    ((256, 256, 256), dict(load_path=7), INVALID),
+    ((256, 256, 256), dict(bm=256, bn=256, stages=3), INVALID),               # no 4-wave 256x256 three-stage kernel
+    ((256, 256, 256), dict(splits=-1), INVALID),
+    ((256, 256, 256), dict(splits=17), INVALID),
+    ((256, 256, 256), dict(load_path=2, stages=2, splits=2), INVALID),        # register path does not split K
+    ((256, 256, 256), dict(persistent=3), INVALID),
+    ((256, 256, 256), dict(group_m=-1), INVALID),
+    ((256, 256, 100), dict(), INVALID),                                       # DMA forced with K % 8 != 0
+    ((256, 256, 256), dict(bm=256, bn=256, stages=5, waves=8, persistent=2), UNSUPPORTED),  # no queue in two-group
+    ((256, 256, 256), dict(bm=256, bn=256, stages=5, persistent=2), UNSUPPORTED),  # ring leaves no queue slot
+    ((16384, 16384, 1024), dict(splits=2), UNSUPPORTED),                      # partial planes above 1 GiB
+])
+def test_config_override_validation(shape, change, status):
+    # every rejected override returns its own status from the host-only selection and from plan
+    # creation, which validates an override before it looks for a device
     import ctypes
-    for conf, st in ((bad, INVALID), (dict(good, stages=5), INVALID), (dict(good, mfma=32), INVALID),
-                     (dict(good, load_path=7), INVALID), (dict(good, bm=256, bn=256, stages=3), INVALID),
-                     (dict(good, splits=-1), INVALID), (dict(good, splits=17), INVALID),
-                     (dict(good, load_path=2, stages=2, splits=2), INVALID)):
-        c = spt.GemmConfig.from_dict(conf)
-        p = ctypes.c_void_p()
-        # without a GPU plan creation stops at the device query; the override is checked after it,
-        # so validate through the same code path the plan uses on the host:
-        assert lib.gemm_plan_create(ctypes.byref(p), 256, 256, 256, F16, F16, F16, 256, 256, 256,
-                                    ctypes.byref(c)) in (st, -3)
+    M, N, K = shape
+    conf = dict(GOOD_OVERRIDE, **change)
+    assert spt.gemm_select_config_status(M, N, K, F16, F16, F16, K, K, N, config=conf) == status
+    c = spt.GemmConfig.from_dict(conf)
+    p = ctypes.c_void_p()
+    assert spt.lib().gemm_plan_create(ctypes.byref(p), M, N, K, F16, F16, F16, K, K, N, ctypes.byref(c)) == status
+    assert not p.value
+
+
+def test_config_override_accepted_and_reported():
+    # a valid override is what the plan launches; the grid comes from the device's CU count
+    c = spt.gemm_select_config(1000, 700, 512, BF16, BF16, F32, 512, 512, 700, config=GOOD_OVERRIDE)
+    assert {k: c[k] for k in ("bm", "bn", "bk", "stages", "waves", "load_path", "splits")} == \
+        {"bm": 128, "bn": 128, "bk": 64, "stages": 4, "waves": 4, "load_path": 1, "splits": 1}
+    assert c["grid"] == min(256, 8 * 6) and c["lds_bytes"] == 4 * 2 * 128 * 64 * 2
+    c = spt.gemm_select_config(1000, 700, 512, BF16, BF16, F32, 512, 512, 700, cu_count=32,
+                               config=dict(GOOD_OVERRIDE, splits=3))
+    assert c["grid"] == 32 and c["splits"] == 3
+    # the staged path on request, where DMA cannot read the rows directly
+    c = spt.gemm_select_config(100, 70, 77, F16, F16, F16, 77, 77, 70, config=dict(GOOD_OVERRIDE, load_path=3))
+    assert c["load_path"] == spt.GEMM_LOAD_STAGED
+    # a good override gets past validation; without a GPU plan creation then stops at the device query
+    import ctypes
+    p = ctypes.c_void_p()
+    st = spt.lib().gemm_plan_create(ctypes.byref(p), 1000, 700, 512, BF16, BF16, F32, 512, 512, 700,
+                                    ctypes.byref(spt.GemmConfig.from_dict(GOOD_OVERRIDE)))
+    assert st == OK or st == -3
+    if st == OK:
+        spt.lib().gemm_plan_destroy(p)
 
 
 # ------------------------------------------------------------------------------ scheduler
