@@ -168,6 +168,29 @@ gemm_status_t gemm_plan_parts(gemm_plan_t plan, int* dim, int64_t* at, gemm_conf
 /* Static, human-readable name of a status code ("GEMM_OK", ...). Never NULL. */
 const char* gemm_status_string(gemm_status_t status);
 
+/*
+ * For callers that cannot allocate device memory (work recorded under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): plan and enqueue C = A·Bᵀ in one call that
+ * calls no allocating routine (no hipMalloc, hipFree or host heap). Arguments and result are those
+ * of gemm_plan_create with a NULL config followed by gemm_run: the same built-in choice, the same
+ * kernels, the same bits. The plan lives on this call's stack. A plan that needs a workspace (a
+ * staged operand copy, split-K partial planes) takes it from a static device array of
+ * GEMM_NOALLOC_SCRATCH_BYTES, which each device holds from the library's first use there until the
+ * process ends; the first call on a device looks up that device's copy (hipGetSymbolAddress), so
+ * make one call outside graph capture before capturing. Every launch writes whatever part of the
+ * array it later reads, so no state carries over from one call to the next.
+ *   The array is shared by every call on a device: calls that overlap on one device (on different
+ *   streams, or from different threads without ordering) race on it and must be ordered by the
+ *   caller. Calls on different devices do not interact.
+ * Errors: those of gemm_plan_create and gemm_run; GEMM_ERR_UNSUPPORTED when the plan's workspace
+ *   exceeds GEMM_NOALLOC_SCRATCH_BYTES (64 MiB: for example a staged copy of more than 64 MiB of
+ *   operands, or split-K partial planes of more than 64 MiB). Nothing is enqueued on an error.
+ */
+#define GEMM_NOALLOC_SCRATCH_BYTES ((int64_t)64 << 20)
+gemm_status_t gemm_run_noalloc(int64_t M, int64_t N, int64_t K, gemm_dtype_t a_dtype, gemm_dtype_t b_dtype,
+                               gemm_dtype_t c_dtype, int64_t lda, int64_t ldb, int64_t ldc, const void* A,
+                               const void* B, void* C, void* stream);
+
 /* ------------------------------------------------------------------------------------------
  * Host-only introspection (no device work). They expose the exact functions the kernels use,
  * so their invariants can be tested without a GPU.

@@ -17,7 +17,7 @@ GEMM_OK, GEMM_ERR_INVALID, GEMM_ERR_UNSUPPORTED, GEMM_ERR_HIP, GEMM_ERR_NOMEM = 
 GEMM_LOAD_AUTO, GEMM_LOAD_DMA, GEMM_LOAD_REG, GEMM_LOAD_STAGED = 0, 1, 2, 3
 
 # every entry point include/gemm.h declares
-EXPORTS = ("gemm_plan_create", "gemm_run", "gemm_plan_destroy", "gemm_plan_describe", "gemm_plan_workspace_bytes",
+EXPORTS = ("gemm_plan_create", "gemm_run", "gemm_run_noalloc", "gemm_plan_destroy", "gemm_plan_describe", "gemm_plan_workspace_bytes",
            "gemm_plan_parts", "gemm_status_string",
            "gemm_select_config", "gemm_select_parts", "gemm_schedule_tile", "gemm_lds_chunk_offset", "gemm_probe_mfma_peak",
            "gemm_probe_copy", "gemm_probe_read", "gemm_probe_lds_read")
@@ -65,6 +65,8 @@ def lib() -> ctypes.CDLL:
     L.gemm_plan_create.argtypes = [P(vp), i64, i64, i64, i32, i32, i32, i64, i64, i64, P(GemmConfig)]
     L.gemm_run.restype = i32
     L.gemm_run.argtypes = [vp, vp, vp, vp, vp]
+    L.gemm_run_noalloc.restype = i32
+    L.gemm_run_noalloc.argtypes = [i64, i64, i64, i32, i32, i32, i64, i64, i64, vp, vp, vp, vp]
     L.gemm_plan_destroy.restype = i32
     L.gemm_plan_destroy.argtypes = [vp]
     L.gemm_plan_describe.restype = i32
@@ -120,6 +122,12 @@ def gemm_plan_create(M: int, N: int, K: int, a_dtype: int, b_dtype: int, c_dtype
 
 def gemm_run(plan: int, a_ptr: int, b_ptr: int, c_ptr: int, stream: int = 0) -> None:
     _check(lib().gemm_run(plan, a_ptr, b_ptr, c_ptr, stream or None), "gemm_run")
+
+
+def gemm_run_noalloc(M: int, N: int, K: int, a_dtype: int, b_dtype: int, c_dtype: int, lda: int, ldb: int, ldc: int,
+                     a_ptr: int, b_ptr: int, c_ptr: int, stream: int = 0) -> None:
+    _check(lib().gemm_run_noalloc(M, N, K, a_dtype, b_dtype, c_dtype, lda, ldb, ldc, a_ptr, b_ptr, c_ptr,
+                                  stream or None), "gemm_run_noalloc")
 
 
 def gemm_plan_destroy(plan: int | None) -> None:

@@ -5,6 +5,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 
 #include "gemm.h"
@@ -403,6 +404,125 @@ gemm_status_t gemm_select_config(int64_t M, int64_t N, int64_t K, gemm_dtype_t a
   return select_impl(M, N, K, a_dtype, b_dtype, c_dtype, lda, ldb, ldc, cu_count, lds_bytes, config, out, nullptr);
 }
 
+}  // extern "C"
+
+namespace {
+
+// Where a plan's parts and workspace come from: the heap and hipMalloc (gemm_plan_create), or,
+// for gemm_run_noalloc, plan records supplied by the caller and the static scratch array.
+struct PlanArena {
+  gemm_plan_s* spare;   // records for the parts of a plan cut in two
+  int spare_left;
+  char* scratch;        // device address of the scratch array (per device)
+  int64_t cap, used;    // its size and the bytes handed out so far (256-byte aligned pieces)
+};
+
+// Fill *p for C[M,N] = A[M,K]·B[N,K]ᵀ on device `dev` (cu compute units, lds bytes of LDS per
+// workgroup). Arguments are already checked. With arena == nullptr, parts are allocated on the heap
+// and the workspace with hipMalloc (freed by gemm_plan_destroy); with an arena, nothing is
+// allocated and a workspace beyond the scratch left is GEMM_ERR_UNSUPPORTED.
+gemm_status_t plan_build(gemm_plan_s* p, int64_t M, int64_t N, int64_t K, gemm_dtype_t a_dtype,
+                         gemm_dtype_t b_dtype, gemm_dtype_t c_dtype, int64_t lda, int64_t ldb, int64_t ldc,
+                         const gemm_config_t* config, int dev, int cu, int lds, PlanArena* arena) {
+  p->M = M; p->N = N; p->K = K; p->lda = lda; p->ldb = ldb; p->ldc = ldc;
+  p->in_dtype = a_dtype; p->out_dtype = c_dtype;
+  p->dev = dev;
+  p->split_dim = -1;
+  p->queue_off = -1;
+  p->ws = nullptr;
+  p->part[0] = p->part[1] = nullptr;
+  gemm_status_t st =
+      select_impl(M, N, K, a_dtype, b_dtype, c_dtype, lda, ldb, ldc, cu, lds, config, &p->cfg, &p->cfg_reg);
+  if (st != GEMM_OK) return st;
+  // the built-in choice may cut the output in two (wave quantisation); each part is a plan over
+  // the operands the kernels read: the staged copies (rows of K rounded up to 8) or A and B
+  const bool staged_path = p->cfg.load_path == GEMM_LOAD_STAGED;
+  Parts parts;
+  if (!config && is_dma(p->cfg.load_path) &&
+      choose_parts(M, N, staged_path ? round_up(K, 8) : K, cu, lds, &parts)) {
+    const int64_t kk = staged_path ? round_up(K, 8) : K;
+    const int64_t la = staged_path ? kk : lda, lb = staged_path ? kk : ldb;
+    const int64_t M0 = parts.dim == 1 ? M : parts.at, N0 = parts.dim == 1 ? parts.at : N;
+    const int64_t M1 = parts.dim == 1 ? M : M - parts.at, N1 = parts.dim == 1 ? N - parts.at : N;
+    const int64_t mm[2] = {M0, M1}, nn[2] = {N0, N1};
+    const gemm_config_t* pc[2] = {&parts.first, &parts.second};
+    for (int i = 0; i < 2 && st == GEMM_OK; ++i) {
+      gemm_plan_s* q = nullptr;
+      if (arena) {
+        if (arena->spare_left < 1) return GEMM_ERR_UNSUPPORTED;
+        q = arena->spare++;
+        --arena->spare_left;
+      } else {
+        q = new (std::nothrow) gemm_plan_s();
+        if (!q) { st = GEMM_ERR_NOMEM; break; }
+      }
+      p->part[i] = q;
+      st = plan_build(q, mm[i], nn[i], kk, a_dtype, b_dtype, c_dtype, la, lb, ldc, pc[i], dev, cu, lds, arena);
+    }
+    if (st != GEMM_OK) return st;
+    p->split_dim = parts.dim;
+    p->split_at = parts.at;
+    p->cfg.splits = 1;  // this plan only stages (when it does); the parts run the mainloops
+  }
+  const bool split = p->cfg.splits > 1;
+  p->fn_main = kernel_fn(p->cfg, a_dtype, split ? GEMM_F32 : c_dtype);
+  p->fn_reg = kernel_fn(p->cfg_reg, a_dtype, c_dtype);
+  p->fn_reduce = split ? spt::splitk_reduce_fn((int)c_dtype) : nullptr;
+  p->fn_stage = p->cfg.load_path == GEMM_LOAD_STAGED ? spt::stage_fn() : nullptr;
+  p->tiles_m = (int)ceil_div(M, p->cfg.bm);
+  p->tiles_n = (int)ceil_div(N, p->cfg.bn);
+  p->tiles_m_reg = (int)ceil_div(M, p->cfg_reg.bm);
+  p->tiles_n_reg = (int)ceil_div(N, p->cfg_reg.bn);
+  if (!p->fn_main) return GEMM_ERR_UNSUPPORTED;
+  const WsLayout w = ws_layout(M, N, K, p->cfg.load_path, p->split_dim >= 0 ? 1 : p->cfg.splits,
+                               p->split_dim < 0 && p->cfg.persistent == 2);
+  p->queue_off = p->split_dim < 0 && p->cfg.persistent == 2 ? w.queue : -1;
+  p->kp = w.kp;
+  p->ldw = w.ldw;
+  p->stage_a_off = w.stage_a;
+  p->stage_b_off = w.stage_b;
+  p->part_off = w.part;
+  if (w.total > 0 && M > 0 && N > 0) {
+    if (arena) {
+      // only the built-in choice runs here, and it never takes the dynamic queue, whose counters
+      // would have to start at zero; every other workspace byte a launch reads it has written
+      if (p->queue_off >= 0) return GEMM_ERR_UNSUPPORTED;
+      const int64_t at = round_up(arena->used, 256);
+      if (at + w.total > arena->cap) return GEMM_ERR_UNSUPPORTED;
+      p->ws = arena->scratch + at;
+      arena->used = at + w.total;
+      return GEMM_OK;
+    }
+    void* ws = nullptr;
+    if (hipMalloc(&ws, (size_t)w.total) != hipSuccess) {
+      (void)hipGetLastError();
+      return GEMM_ERR_NOMEM;
+    }
+    p->ws = (char*)ws;
+    // the queue counters start at zero; each launch leaves them at zero again
+    if (p->queue_off >= 0 && hipMemset(p->ws + p->queue_off, 0, 8) != hipSuccess) {
+      (void)hipGetLastError();
+      return GEMM_ERR_HIP;
+    }
+  }
+  return GEMM_OK;
+}
+
+// The current device, its CU count and LDS per workgroup; GEMM_ERR_HIP unless it is a gfx950.
+gemm_status_t device_info(int* dev, int* cu, int* lds) {
+  if (hipGetDevice(dev) != hipSuccess) return GEMM_ERR_HIP;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, *dev) != hipSuccess) return GEMM_ERR_HIP;
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return GEMM_ERR_HIP;
+  *cu = prop.multiProcessorCount;
+  *lds = (int)(prop.sharedMemPerBlock < (size_t)kMaxLds ? prop.sharedMemPerBlock : (size_t)kMaxLds);
+  return GEMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 gemm_status_t gemm_plan_create(gemm_plan_t* out, int64_t M, int64_t N, int64_t K, gemm_dtype_t a_dtype,
                                gemm_dtype_t b_dtype, gemm_dtype_t c_dtype, int64_t lda, int64_t ldb, int64_t ldc,
                                const gemm_config_t* config) {
@@ -418,79 +538,15 @@ gemm_status_t gemm_plan_create(gemm_plan_t* out, int64_t M, int64_t N, int64_t K
                      nullptr);
     if (st != GEMM_OK) return st;
   }
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return GEMM_ERR_HIP;
-  hipDeviceProp_t prop;
-  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return GEMM_ERR_HIP;
-  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return GEMM_ERR_HIP;
-  const int cu = prop.multiProcessorCount;
-  const int lds = (int)(prop.sharedMemPerBlock < (size_t)kMaxLds ? prop.sharedMemPerBlock : (size_t)kMaxLds);
-
+  int dev = 0, cu = 0, lds = 0;
+  st = device_info(&dev, &cu, &lds);
+  if (st != GEMM_OK) return st;
   gemm_plan_s* p = new (std::nothrow) gemm_plan_s();
   if (!p) return GEMM_ERR_NOMEM;
-  p->M = M; p->N = N; p->K = K; p->lda = lda; p->ldb = ldb; p->ldc = ldc;
-  p->in_dtype = a_dtype; p->out_dtype = c_dtype;
-  p->dev = dev;
-  p->split_dim = -1;
-  p->queue_off = -1;
-  st = select_impl(M, N, K, a_dtype, b_dtype, c_dtype, lda, ldb, ldc, cu, lds, config, &p->cfg, &p->cfg_reg);
-  if (st != GEMM_OK) { delete p; return st; }
-  // the built-in choice may cut the output in two (wave quantisation); each part is a plan over
-  // the operands the kernels read: the staged copies (rows of K rounded up to 8) or A and B
-  const bool staged_path = p->cfg.load_path == GEMM_LOAD_STAGED;
-  Parts parts;
-  if (!config && is_dma(p->cfg.load_path) &&
-      choose_parts(M, N, staged_path ? round_up(K, 8) : K, cu, lds, &parts)) {
-    const int64_t kk = staged_path ? round_up(K, 8) : K;
-    const int64_t la = staged_path ? kk : lda, lb = staged_path ? kk : ldb;
-    const int64_t M0 = parts.dim == 1 ? M : parts.at, N0 = parts.dim == 1 ? parts.at : N;
-    const int64_t M1 = parts.dim == 1 ? M : M - parts.at, N1 = parts.dim == 1 ? N - parts.at : N;
-    st = gemm_plan_create(&p->part[0], M0, N0, kk, a_dtype, b_dtype, c_dtype, la, lb, ldc, &parts.first);
-    if (st == GEMM_OK)
-      st = gemm_plan_create(&p->part[1], M1, N1, kk, a_dtype, b_dtype, c_dtype, la, lb, ldc, &parts.second);
-    if (st != GEMM_OK) {
-      (void)gemm_plan_destroy(p->part[0]);
-      delete p;
-      return st;
-    }
-    p->split_dim = parts.dim;
-    p->split_at = parts.at;
-    p->cfg.splits = 1;  // this plan only stages (when it does); the parts run the mainloops
-  }
-  const bool split = p->cfg.splits > 1;
-  p->fn_main = kernel_fn(p->cfg, a_dtype, split ? GEMM_F32 : c_dtype);
-  p->fn_reg = kernel_fn(p->cfg_reg, a_dtype, c_dtype);
-  p->fn_reduce = split ? spt::splitk_reduce_fn((int)c_dtype) : nullptr;
-  p->fn_stage = p->cfg.load_path == GEMM_LOAD_STAGED ? spt::stage_fn() : nullptr;
-  p->tiles_m = (int)ceil_div(M, p->cfg.bm);
-  p->tiles_n = (int)ceil_div(N, p->cfg.bn);
-  p->tiles_m_reg = (int)ceil_div(M, p->cfg_reg.bm);
-  p->tiles_n_reg = (int)ceil_div(N, p->cfg_reg.bn);
-  if (!p->fn_main) { delete p; return GEMM_ERR_UNSUPPORTED; }
-  const WsLayout w = ws_layout(M, N, K, p->cfg.load_path, p->split_dim >= 0 ? 1 : p->cfg.splits,
-                               p->split_dim < 0 && p->cfg.persistent == 2);
-  p->queue_off = p->split_dim < 0 && p->cfg.persistent == 2 ? w.queue : -1;
-  p->kp = w.kp;
-  p->ldw = w.ldw;
-  p->stage_a_off = w.stage_a;
-  p->stage_b_off = w.stage_b;
-  p->part_off = w.part;
-  if (w.total > 0 && M > 0 && N > 0) {
-    void* ws = nullptr;
-    if (hipMalloc(&ws, (size_t)w.total) != hipSuccess) {
-      (void)hipGetLastError();
-      (void)gemm_plan_destroy(p->part[0]);
-      (void)gemm_plan_destroy(p->part[1]);
-      delete p;
-      return GEMM_ERR_NOMEM;
-    }
-    p->ws = (char*)ws;
-    // the queue counters start at zero; each launch leaves them at zero again
-    if (p->queue_off >= 0 && hipMemset(p->ws + p->queue_off, 0, 8) != hipSuccess) {
-      (void)hipGetLastError();
-      (void)gemm_plan_destroy(p);
-      return GEMM_ERR_HIP;
-    }
+  st = plan_build(p, M, N, K, a_dtype, b_dtype, c_dtype, lda, ldb, ldc, config, dev, cu, lds, nullptr);
+  if (st != GEMM_OK) {
+    (void)gemm_plan_destroy(p);
+    return st;
   }
   *out = p;
   return GEMM_OK;
@@ -662,6 +718,74 @@ gemm_status_t gemm_run(gemm_plan_t plan, const void* A, const void* B, void* C, 
   r.C = C;
   r.ldc = (int)plan->ldc;
   return launch(plan->fn_reduce, stream_grid(plan->M * ceil_div(plan->N, 8)), 256, &r, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------------------------
+// The no-allocation entry point. Its workspace (staged operand copies, split-K partial planes) is
+// this file-scope device array: each device that runs it holds its own copy from the library's
+// first use on that device until the process ends. Host code reaches a device's copy only through
+// the address hipGetSymbolAddress returns with that device current (the array's name is a host-side
+// stand-in, not a device address).
+constexpr int64_t kScratchBytes = GEMM_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+struct ScratchDevice {
+  bool ready;
+  int cu, lds;
+  char* ptr;  // this device's copy of `scratch`
+};
+ScratchDevice g_scratch_dev[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The current device's properties and scratch address, found on its first use.
+gemm_status_t scratch_device(int* dev, int* cu, int* lds, char** ptr) {
+  if (hipGetDevice(dev) != hipSuccess) return GEMM_ERR_HIP;
+  if (*dev < 0 || *dev >= kMaxDevices) return GEMM_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  ScratchDevice& d = g_scratch_dev[*dev];
+  if (!d.ready) {
+    int dv = 0;
+    const gemm_status_t st = device_info(&dv, &d.cu, &d.lds);
+    if (st != GEMM_OK) return st;
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return GEMM_ERR_HIP;
+    }
+    d.ptr = (char*)p;
+    d.ready = true;
+  }
+  *cu = d.cu;
+  *lds = d.lds;
+  *ptr = d.ptr;
+  return GEMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gemm_status_t gemm_run_noalloc(int64_t M, int64_t N, int64_t K, gemm_dtype_t a_dtype, gemm_dtype_t b_dtype,
+                               gemm_dtype_t c_dtype, int64_t lda, int64_t ldb, int64_t ldc, const void* A,
+                               const void* B, void* C, void* stream) {
+  gemm_status_t st = check_args(M, N, K, a_dtype, b_dtype, c_dtype, lda, ldb, ldc);
+  if (st != GEMM_OK) return st;
+  if (M == 0 || N == 0) return GEMM_OK;
+  if (!C || (K > 0 && (!A || !B))) return GEMM_ERR_INVALID;
+  int dev = 0, cu = 0, lds = 0;
+  char* sp = nullptr;
+  st = scratch_device(&dev, &cu, &lds, &sp);
+  if (st != GEMM_OK) return st;
+  gemm_plan_s plans[3] = {};  // the plan and the two parts of a plan cut in two, on this stack
+  PlanArena arena{plans + 1, 2, sp, kScratchBytes, 0};
+  st = plan_build(&plans[0], M, N, K, a_dtype, b_dtype, c_dtype, lda, ldb, ldc, nullptr, dev, cu, lds, &arena);
+  if (st != GEMM_OK) return st;
+  return gemm_run(&plans[0], A, B, C, stream);
 }
 
 int gemm_schedule_tile(int64_t tiles_m, int64_t tiles_n, int splits, int group_m, int grid, int wg, int round,
