@@ -242,7 +242,7 @@ struct TileShape {
   static constexpr int LA = A_INSTR / W, LB = B_INSTR / W, LW = LA + LB;   // per wave, per stage
   static constexpr int MAX_VM = SPLIT ? 2 * LA + LB : LW * (S > 1 ? S - 1 : 1);  // largest vmcnt threshold
   static_assert(BK == 32 || BK == 64 || BK == 128, "K-tile is one 64-byte row or one or two 128-byte groups");
-  static_assert(S >= 1 && S <= (BK == 128 ? 4 : 5), "1..4 stages (5 slots for 32- or 64-deep K-tiles)");
+  static_assert(S >= 1 && S <= (BK == 128 ? 8 : 5), "1..5 stages (up to 8 for 128-deep K-tiles)");
   static_assert(!SPLIT || A_BYTES == B_BYTES, "split ring: A and B tiles fill equal slots");
   static_assert(TM % 16 == 0 && TN % 32 == 0, "wave tile: 16-row A fragments, pairs of 16-row B fragments");
   static_assert(A_INSTR % W == 0 && B_INSTR % W == 0, "every wave issues the same number of loads");

@@ -185,19 +185,27 @@ __global__ void __launch_bounds__(WM* WN * 64, 1) gemm_dma_kernel(GemmArgs args)
     auto kstep = [&](int buf, auto zero_c, auto nr_c, auto nd_c, auto&& rd, auto&& dm) {
       constexpr bool kZero = decltype(zero_c)::value;
       constexpr int NR = decltype(nr_c)::value, ND = decltype(nd_c)::value;
-      static_assert(NR <= NM && ND <= NM, "at most one read and one DMA per MFMA slot");
       static_for<NM>([&](auto m_c) {
         constexpr int m = decltype(m_c)::value;
         constexpr int i = m / T::FM, j = m % T::FM;
         acc[i][j] = mfma16<TIn>(xf[buf][i], yf[buf][j], kZero ? zero4 : acc[i][j]);
-        // load slots: the reads, and separately the DMAs, are spread evenly over the MFMA slots
-        if constexpr (NR > 0) {
+        // load slots: the reads, and separately the DMAs, are spread evenly over the MFMA slots. With
+        // more of them than MFMAs (the small skinny tiles) slot m takes reads [m*NR/NM, (m+1)*NR/NM)
+        if constexpr (NR > 0 && NR <= NM) {
           constexpr int sr = NM / NR;
           if constexpr (m % sr == 0 && m / sr < NR) rd(m / sr);
+        } else if constexpr (NR > NM) {
+          static_for<NR>([&](auto r_c) {
+            if constexpr (decltype(r_c)::value * NM / NR == m) rd(decltype(r_c)::value);
+          });
         }
-        if constexpr (ND > 0) {
+        if constexpr (ND > 0 && ND <= NM) {
           constexpr int sd = NM / ND;
           if constexpr (m % sd == sd / 2 && m / sd < ND) dm(m / sd);
+        } else if constexpr (ND > NM) {
+          static_for<ND>([&](auto d_c) {
+            if constexpr (decltype(d_c)::value * NM / ND == m) dm(decltype(d_c)::value);
+          });
         }
         __builtin_amdgcn_sched_barrier(0);
       });
@@ -406,6 +414,10 @@ const KernelEntry* dma_kernel_table(int* count) {
       make_entry<64, 64, 64, 4, 2, 2>(),
       make_entry<64, 64, 128, 4, 2, 2>(),
       make_entry<64, 64, 64, 2, 2, 2>(),
+      // skinny shapes (M of a few dozen rows): a 32x32 tile with 128-deep K-tiles and two waves keeps
+      // one workgroup per 32 columns streaming, with up to seven 8 KiB operand tiles of B in flight
+      make_entry<32, 32, 128, 4, 2, 1>(),
+      make_entry<32, 32, 128, 8, 2, 1>(),
   };
   *count = (int)(sizeof(table) / sizeof(table[0]));
   return table;

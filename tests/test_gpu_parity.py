@@ -149,6 +149,23 @@ def test_deep_64_tile_bit_exact(K, persistent):
         check_full(a, b, K, si.F16, si.F32, c, N, exact=True)
 
 
+@pytest.mark.parametrize("K", [8, 128, 136, 512, 896, 1032, 1024 + 8 * 128 + 40])
+@pytest.mark.parametrize("s", [4, 8])
+@pytest.mark.parametrize("persistent,splits", [(1, 1), (0, 1), (1, 3)])
+def test_skinny_32_tile_bit_exact(K, s, persistent, splits):
+    # the 32x32 tile with 128-deep K-tiles (two waves; four or eight stages, several reads and loads
+    # per MFMA slot): fewer K-tiles than stages, about as many, and more; K tails inside either
+    # 64-wide group; M = 32 exactly as in the skinny workload, and a ragged 3 x 2 grid
+    for M, N in ((32, 5 * 32 - 9), (2 * 32 + 13, 2 * 32 - 5)):
+        a = ints(M, K, si.F16, 60 + K + M + s)
+        b = ints(N, K, si.F16, 61 + K + N + s)
+        c, desc = run_gpu(a, b, K, si.F16, si.F32,
+                          config=cfg(32, 32, s, bk=128, waves=2, persistent=persistent, splits=splits,
+                                     grid=2 if persistent else 0))
+        assert (desc["bm"], desc["bn"], desc["bk"], desc["stages"], desc["waves"]) == (32, 32, 128, s, 2)
+        check_full(a, b, K, si.F16, si.F32, c, N, exact=True)
+
+
 @pytest.mark.parametrize("bm,bn,s", REG_CONFIGS)
 def test_reg_configs_bit_exact(bm, bn, s):
     M, N, K = 2 * bm + 7, bn + 9, 3 * 64 + 13  # K not a multiple of 8: element-masked tail

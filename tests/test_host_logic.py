@@ -114,9 +114,10 @@ def test_config_choice(name):
         assert units >= 256 and c["splits"] > 1  # too few tiles for 256 CUs: K is split to fill them
     if name == "c5a":
         # M = 32: a larger tile would be mostly padding. The time is B streaming in at the HBM rate;
-        # 128 workgroups with 128-deep K-tiles keep enough bytes in flight for that, so K stays whole
-        # and no partial planes are written and reduced
-        assert (c["bm"], c["bn"], c["bk"], c["stages"]) == (64, 64, 128, 4) and c["splits"] == 1
+        # 256 workgroups of 32x32 tiles with 128-deep K-tiles stream it (one per 32 columns), so K
+        # stays whole and no partial planes are written and reduced
+        assert (c["bm"], c["bn"], c["bk"], c["stages"], c["waves"]) == (32, 32, 128, 4, 2) and c["splits"] == 1
+        assert c["grid"] == 256
 
 
 def test_staging_needs_each_source_under_2gib():
@@ -338,7 +339,7 @@ DMA_TABLE = [(256, 256, 2), (256, 256, 1), (256, 128, 3), (256, 128, 2), (256, 1
              (128, 128, 3), (128, 128, 2), (128, 128, 1), (64, 64, 4), (64, 64, 2)]
 # (bm, bn, bk, stages, waves) of the configurations with their own ring shape
 RING_TABLE = [(256, 256, 64, 5, 4), (256, 256, 32, 4, 4), (256, 256, 64, 5, 8), (256, 256, 64, 2, 8),
-              (64, 64, 128, 4, 4)]
+              (64, 64, 128, 4, 4), (32, 32, 128, 4, 2), (32, 32, 128, 8, 2)]
 
 
 def stage_bytes(bm, bn, bk, elem=2):
