@@ -230,6 +230,18 @@ int gemm_schedule_tile(int64_t tiles_m, int64_t tiles_n, int splits, int group_m
                        int round, int64_t* tm, int64_t* tn, int* split);
 
 /*
+ * The pipeline protocol's counts for the DMA kernel with this tile (bm, bn, bk), ring depth and wave
+ * count, as the kernel uses them ("GEMM II — pipelining with TMA", Step 5; "Multi-Stage Software
+ * Pipelining", Prefill and Main loop): out[0..9] = loads per wave of an A operand tile, of a B
+ * operand tile, of a stage; 1 for the split ring of five operand slots; the vmcnt threshold after the
+ * prologue and at each hand-over; the refill loads issued in the hand-over k-step and in k-step 0 of
+ * the next K-tile; and, for the two-group kernel (waves 8), the first group's threshold after its
+ * prologue and the second group's after a memory phase in which it loaded. Returns 10, or -1 when
+ * no DMA kernel has this shape or out is NULL or n_out < 10.
+ */
+int gemm_pipeline_protocol(int bm, int bn, int bk, int stages, int waves, int* out, int n_out);
+
+/*
  * Byte offset, inside one LDS operand tile of `rows` rows and depth bk (32, 64 or 128), of the
  * 16-byte chunk holding elements [8*chunk, 8*chunk + 8) of tile row `row` (the XOR swizzle:
  * 128-byte rows with chunk XOR (row mod 8) for bk 64 and 128, 64-byte rows with chunk XOR

@@ -7,7 +7,7 @@ from ._lib import (EXPORTS, GEMM_BF16, GEMM_F16, GEMM_F32, GEMM_LOAD_AUTO, GEMM_
                    GEMM_LOAD_STAGED, GemmConfig, GemmError, GemmLibraryMissing, gemm_lds_chunk_offset,
                    gemm_plan_create, gemm_plan_describe, gemm_plan_destroy, gemm_plan_parts, gemm_plan_workspace_bytes,
                    gemm_probe_copy, gemm_probe_lds_read, gemm_probe_mfma_peak, gemm_probe_read, gemm_run, gemm_run_noalloc,
-                   gemm_schedule_tile, gemm_select_config, gemm_select_config_status, gemm_select_parts, lib,
+                   gemm_pipeline_protocol, gemm_schedule_tile, gemm_select_config, gemm_select_config_status, gemm_select_parts, lib,
                    status_string)
 from .torch_api import Plan, matmul
 
@@ -15,5 +15,5 @@ __all__ = ["EXPORTS", "GEMM_BF16", "GEMM_F16", "GEMM_F32", "GEMM_LOAD_AUTO", "GE
            "GEMM_LOAD_STAGED", "GemmConfig", "GemmError", "GemmLibraryMissing", "Plan", "gemm_lds_chunk_offset",
            "gemm_plan_create", "gemm_plan_describe", "gemm_plan_destroy", "gemm_plan_parts", "gemm_plan_workspace_bytes",
            "gemm_probe_copy", "gemm_probe_lds_read", "gemm_probe_mfma_peak", "gemm_probe_read", "gemm_run", "gemm_run_noalloc",
-           "gemm_schedule_tile", "gemm_select_config", "gemm_select_config_status", "gemm_select_parts", "lib", "matmul",
+           "gemm_pipeline_protocol", "gemm_schedule_tile", "gemm_select_config", "gemm_select_config_status", "gemm_select_parts", "lib", "matmul",
            "status_string"]

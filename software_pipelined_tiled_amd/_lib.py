@@ -19,7 +19,7 @@ GEMM_LOAD_AUTO, GEMM_LOAD_DMA, GEMM_LOAD_REG, GEMM_LOAD_STAGED = 0, 1, 2, 3
 # every entry point include/gemm.h declares
 EXPORTS = ("gemm_plan_create", "gemm_run", "gemm_run_noalloc", "gemm_plan_destroy", "gemm_plan_describe", "gemm_plan_workspace_bytes",
            "gemm_plan_parts", "gemm_status_string",
-           "gemm_select_config", "gemm_select_parts", "gemm_schedule_tile", "gemm_lds_chunk_offset", "gemm_probe_mfma_peak",
+           "gemm_select_config", "gemm_select_parts", "gemm_schedule_tile", "gemm_pipeline_protocol", "gemm_lds_chunk_offset", "gemm_probe_mfma_peak",
            "gemm_probe_copy", "gemm_probe_read", "gemm_probe_lds_read")
 
 
@@ -85,6 +85,8 @@ def lib() -> ctypes.CDLL:
                                      P(GemmConfig)]
     L.gemm_schedule_tile.restype = i32
     L.gemm_schedule_tile.argtypes = [i64, i64, i32, i32, i32, i32, i32, P(i64), P(i64), P(i32)]
+    L.gemm_pipeline_protocol.restype = i32
+    L.gemm_pipeline_protocol.argtypes = [i32, i32, i32, i32, i32, P(i32), i32]
     L.gemm_lds_chunk_offset.restype = i64
     L.gemm_lds_chunk_offset.argtypes = [i32, i32, i32, i32]
     L.gemm_probe_mfma_peak.restype = i32
@@ -200,6 +202,17 @@ def gemm_schedule_tile(tiles_m, tiles_n, splits, group_m, grid, wg, rnd):
     if r < 0:
         raise GemmError(GEMM_ERR_INVALID, "gemm_schedule_tile")
     return (tm.value, tn.value, sp.value) if r == 1 else None
+
+
+PROTOCOL_FIELDS = ("la", "lb", "lw", "split", "prologue_wait", "handover_wait", "refill_now", "refill_later",
+                   "pp_g0_prologue_wait", "pp_g1_wait")
+
+
+def gemm_pipeline_protocol(bm: int, bn: int, bk: int, stages: int, waves: int) -> dict | None:
+    """The kernel's pipeline counts for this shape (None if no DMA kernel has it)."""
+    out = (ctypes.c_int * 10)()
+    n = lib().gemm_pipeline_protocol(bm, bn, bk, stages, waves, out, 10)
+    return dict(zip(PROTOCOL_FIELDS, out)) if n == 10 else None
 
 
 def gemm_lds_chunk_offset(rows: int, bk: int, row: int, chunk: int) -> int:

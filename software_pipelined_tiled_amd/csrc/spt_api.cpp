@@ -823,6 +823,18 @@ int gemm_schedule_tile(int64_t tiles_m, int64_t tiles_n, int splits, int group_m
   return 1;
 }
 
+int gemm_pipeline_protocol(int bm, int bn, int bk, int stages, int waves, int* out, int n_out) {
+  if (!out || n_out < 10) return -1;
+  gemm_config_t c{};
+  c.bm = bm; c.bn = bn; c.bk = bk; c.stages = stages; c.waves = waves; c.mfma = 16; c.load_path = GEMM_LOAD_DMA;
+  if (!find_entry_for_path(c)) return -1;
+  const spt::PipeProtocol p = spt::pipe_protocol(bm, bn, bk, stages, waves);
+  const int v[10] = {p.la, p.lb, p.lw, p.split, p.prologue_wait, p.handover_wait, p.refill_now, p.refill_later,
+                     p.pp_g0_prologue_wait, p.pp_g1_wait};
+  for (int i = 0; i < 10; ++i) out[i] = v[i];
+  return 10;
+}
+
 int64_t gemm_lds_chunk_offset(int rows, int bk, int row, int chunk) {
   if ((bk != 32 && bk != 64 && bk != 128) || rows < 1 || row < 0 || row >= rows || chunk < 0 || chunk >= bk / 8)
     return -1;

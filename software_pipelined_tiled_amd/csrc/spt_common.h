@@ -104,6 +104,60 @@ SPT_HD void unit_decode(int t, int tiles_m, int tiles_n, int group_m, int& tm, i
   grouped_raster(t - s * per, tiles_m, tiles_n, group_m, tm, tn);
 }
 
+// ---------------------------------------------------------------------------------------------
+// The pipeline protocol's counts ("GEMM II — pipelining with TMA", Step 5: loads run ahead of the
+// math through a ring of stages; "Multi-Stage Software Pipelining", Prefill and Main loop). Each
+// wave issues its share of every operand tile as 1 KiB direct global->LDS loads; a wave knows a
+// K-tile has landed when at most `n` of its own loads are outstanding (s_waitcnt vmcnt(n)), and the
+// barrier after that wait publishes every wave's share. The kernels take every wait threshold and
+// every refill count from these functions, and the host-only introspection returns the same
+// values, so the CPU replays of the protocol check the numbers the kernels run with.
+//
+// The 4-wave DMA kernel (waves <= 4), per K-tile k:
+//   prologue: the first S K-tiles (split ring: operand tiles A0 B0 A1 B1 A2) are loaded, then the
+//             wave waits until K-tile 0 has landed: vmcnt(prologue_wait);
+//   hand-over (before the last k-step of K-tile k): vmcnt(handover_wait) = K-tile k+1 landed, with
+//             only later K-tiles in flight; then the barrier frees K-tile k's slots, and the refill
+//             (K-tile k+S, or the split ring's next operand tiles) is issued: `refill_now` loads in
+//             the hand-over k-step and `refill_later` in k-step 0 of the next K-tile.
+// The two-group kernel (waves = 8, bm = bn = 256, bk = 64): an operand tile is `la` loads of one
+// group; G0 waits vmcnt(pp_g0_prologue_wait) after its prologue (A0, B0, A1) and vmcnt(0) after each
+// compute phase; G1 waits vmcnt(pp_g1_wait) after the memory phase in which it loaded A(g+2), else 0.
+struct PipeProtocol {
+  int la, lb, lw;       // loads per wave: an A tile, a B tile, a stage
+  int split;            // five operand slots of one K-tile each (bk 64, S 5, square tile)
+  int prologue_wait;
+  int handover_wait;
+  int refill_now, refill_later;
+  int pp_g0_prologue_wait, pp_g1_wait;
+  int max_wait;         // the largest threshold (vmcnt is a 6-bit counter)
+};
+
+SPT_HD constexpr PipeProtocol pipe_protocol(int bm, int bn, int bk, int s, int waves) {
+  PipeProtocol p{};
+  const int issuers = waves == 8 ? 4 : waves;  // two-group kernel: one group of four loads a tile
+  p.la = bm * bk * 2 / 1024 / issuers;
+  p.lb = bn * bk * 2 / 1024 / issuers;
+  p.lw = p.la + p.lb;
+  p.split = (bk == 64 && s == 5 && bm == bn) ? 1 : 0;
+  const int nsub = bk / 32;  // MFMA k-steps per K-tile
+  if (p.split) {
+    p.prologue_wait = 2 * p.la + p.lb;  // A1 and B1 ... beyond A0 B0: only tiles after K-tile 0 outstanding
+    p.handover_wait = p.la;             // only the next-but-one K-tile's A tile may be in flight
+    p.refill_now = p.lb;
+    p.refill_later = p.la;
+  } else {
+    p.prologue_wait = p.lw * (s > 1 ? s - 1 : 0);
+    p.handover_wait = s > 1 ? p.lw * (s - 2) : 0;
+    p.refill_now = s > 2 && nsub > 1 ? p.lw / 2 : (s >= 2 ? p.lw : 0);
+    p.refill_later = s >= 2 ? p.lw - p.refill_now : 0;
+  }
+  p.pp_g0_prologue_wait = p.split ? p.la : 0;
+  p.pp_g1_wait = p.split ? p.la : 0;
+  p.max_wait = p.prologue_wait;
+  return p;
+}
+
 // Kernel arguments (passed by value).
 struct GemmArgs {
   const void* A;

@@ -239,8 +239,10 @@ struct TileShape {
   static constexpr int SLOT = A_BYTES;
   static constexpr int LDS = SPLIT ? S * SLOT : S * STAGE;
   static constexpr int A_INSTR = A_BYTES / 1024, B_INSTR = B_BYTES / 1024;  // 1 KiB per DMA instruction
-  static constexpr int LA = A_INSTR / W, LB = B_INSTR / W, LW = LA + LB;   // per wave, per stage
-  static constexpr int MAX_VM = SPLIT ? 2 * LA + LB : LW * (S > 1 ? S - 1 : 1);  // largest vmcnt threshold
+  static constexpr PipeProtocol P = pipe_protocol(BM, BN, BK, S, W);
+  static constexpr int LA = P.la, LB = P.lb, LW = P.lw;   // per wave, per stage
+  static constexpr int MAX_VM = P.max_wait;               // largest vmcnt threshold
+  static_assert(LA == A_INSTR / W && LB == B_INSTR / W && (P.split != 0) == SPLIT, "protocol and tile agree");
   static_assert(BK == 32 || BK == 64 || BK == 128, "K-tile is one 64-byte row or one or two 128-byte groups");
   static_assert(S >= 1 && S <= (BK == 128 ? 8 : 5), "1..5 stages (up to 8 for 128-deep K-tiles)");
   static_assert(!SPLIT || A_BYTES == B_BYTES, "split ring: A and B tiles fill equal slots");

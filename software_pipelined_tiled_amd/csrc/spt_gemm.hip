@@ -228,8 +228,8 @@ __global__ void __launch_bounds__(WM* WN * 64, 1) gemm_dma_kernel(GemmArgs args)
     // have landed and only tile k+2's A tile may still be in flight: vmcnt(LA).
     // kFirst: the first tile, whose MFMA chains start from zero. b0_c: the fragment buffer the
     // tile's k-step 0 uses (the k-step parity; it alternates per tile when a tile is one k-step).
-    constexpr int LW1 = T::SPLIT ? T::LB : (S > 2 && T::NSUB > 1 ? T::LW / 2 : (S >= 2 ? T::LW : 0));
-    constexpr int LWD = T::SPLIT ? T::LA : T::LW - LW1;  // deferred loads, in k-step 0 of the next tile
+    constexpr int LW1 = T::P.refill_now;
+    constexpr int LWD = T::P.refill_later;  // deferred loads, in k-step 0 of the next tile
     auto k_tile = [&](int k, int pos, auto first_c, auto handover_c, auto b0_c) {
       constexpr bool kFirst = decltype(first_c)::value;
       constexpr bool kHandover = decltype(handover_c)::value;
@@ -261,7 +261,7 @@ __global__ void __launch_bounds__(WM* WN * 64, 1) gemm_dma_kernel(GemmArgs args)
           } else {
             // plain ring: every hand-over issued LW loads, so exactly tiles k+2 .. k+S-1 may still be
             // in flight; split ring: tile k+2's A tile
-            wait_vmcnt<T::SPLIT ? T::LA : T::LW * (S - 2)>();
+            wait_vmcnt<T::P.handover_wait>();
             barrier_sync();  // tile k+1 visible to all waves; tile k's slots free in all waves
             static_assert(T::NSUB >= 2 || LW1 == T::LW, "the deferred half needs a k-step before the hand-over");
             kstep(buf, zero_c, nr_c, std::integral_constant<int, LW1>{},
@@ -304,11 +304,11 @@ __global__ void __launch_bounds__(WM* WN * 64, 1) gemm_dma_kernel(GemmArgs args)
 #pragma unroll
         for (int d = 0; d < (h % 2 ? T::LB : T::LA); ++d)
           dma_one(Regions{h * T::SLOT, h * T::SLOT}, h / 2, (h % 2 ? T::LA : 0) + d);
-      wait_vmcnt<2 * T::LA + T::LB>();  // this wave's part of tile 0 landed
+      wait_vmcnt<T::P.prologue_wait>();  // this wave's part of tile 0 landed
     } else {
 #pragma unroll
       for (int s = 0; s < S; ++s) issue(regions(s), s);
-      wait_vmcnt<T::LW * (S - 1)>();  // this wave's part of tile 0 landed
+      wait_vmcnt<T::P.prologue_wait>();  // this wave's part of tile 0 landed
     }
     barrier_sync();  // ... and every wave's
     read_frags(regions(0), 0, 0);

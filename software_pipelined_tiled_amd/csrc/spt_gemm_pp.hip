@@ -77,7 +77,9 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmArgs args) {
   static_assert(MF == 16 || MF == 32, "16x16x32 or 32x32x16 MFMA");
   constexpr int A_BYTES = BM * BK * 2, STAGE = (BM + BN) * BK * 2;
   constexpr int LDS = SPLIT ? S * A_BYTES : S * STAGE;
-  constexpr int LA = A_BYTES / 1024 / 4, LB = LA;    // DMA instructions per wave for one operand tile
+  constexpr PipeProtocol P = pipe_protocol(BM, BN, BK, S, 8);
+  constexpr int LA = P.la, LB = P.lb;                // DMA instructions per wave for one operand tile
+  static_assert(LA == A_BYTES / 1024 / 4 && LB == LA, "one group of four waves loads an operand tile");
   static_assert(S == 2 || S == 5, "two 64 KiB stages or five 32 KiB operand slots");
   static_assert(LDS <= 160 * 1024, "LDS ring fits the 160 KiB of a CU");
   __shared__ __attribute__((aligned(1024))) char smem[LDS];
@@ -373,7 +375,7 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmArgs args) {
     issue_b(cur, b_at(0));
     if (SPLIT && valid(nx)) {
       issue_a(nx, a_at(pos_step(0, 1)));
-      wait_vmcnt<LA>();  // K-tile 0 landed; A(1) may be in flight
+      wait_vmcnt<P.pp_g0_prologue_wait>();  // K-tile 0 landed; A(1) may be in flight
     } else {
       wait_vmcnt<0>();
     }
@@ -441,7 +443,7 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmArgs args) {
       // A(g+1) landed: only the loads of A(g+2) may still be in flight
       auto wait_a = [&]() SPT_INLINE {
         if constexpr (SPLIT) {
-          if (loaded) wait_vmcnt<LA>();
+          if (loaded) wait_vmcnt<P.pp_g1_wait>();
           else wait_vmcnt<0>();
         }
       };

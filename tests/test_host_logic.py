@@ -382,146 +382,184 @@ def test_stage_accounting_of_ring_configs(bm, bn, bk, s, waves):
 
 
 # ------------------------------------------------------------------------------ ring protocol replay
+#
+# The replays below take every wait threshold and refill count from gemm_pipeline_protocol, which
+# returns the constants the kernels are compiled with (both read the same constexpr function), so a
+# threshold that would let a wave read a K-tile before it landed, or refill a slot another wave is
+# still reading, fails here without a GPU.
 
-def replay_ring(KT, S, LW, wait_slack=0, refill_before_barrier=False):
-    """Replay the K-loop schedule of the DMA kernel for one wave (all waves are symmetric, and a
-    barrier is a point all of them reach). Loads complete in issue order; a wait vmcnt(n) returns
-    when at most n of this wave's loads are outstanding. Checks: a tile is read only after its
-    loads completed, and a slot is refilled only after every read of its previous tile."""
-    issued = []          # tile of each issued load, in order
-    slot_tile = {}       # slot -> tile it holds (or will hold)
-    reads_done = set()   # tiles whose fragment reads have completed (lgkmcnt(0) + barrier)
-    landed_upto = -1     # loads [0, landed_upto] complete
+# (bm, bn, bk, stages, waves) of every DMA mainloop kernel
+PLAIN_KERNELS = [(256, 256, 64, 2, 4), (256, 256, 32, 4, 4), (256, 256, 64, 1, 4), (256, 128, 64, 3, 4),
+                 (256, 128, 64, 2, 4), (256, 128, 64, 1, 4), (128, 128, 64, 4, 4), (128, 128, 64, 3, 4),
+                 (128, 128, 64, 2, 4), (128, 128, 64, 1, 4), (64, 64, 64, 4, 4), (64, 64, 128, 4, 4),
+                 (64, 64, 64, 2, 4), (32, 32, 128, 4, 2), (32, 32, 128, 8, 2)]
+SPLIT_KERNELS = [(256, 256, 64, 5, 4)]
+TWO_GROUP_KERNELS = [(256, 256, 64, 5, 8), (256, 256, 64, 2, 8)]
 
-    def issue(slot, tile):
-        prev = slot_tile.get(slot)
-        assert prev is None or prev in reads_done, f"slot {slot} refilled with tile {tile} before tile {prev} was read"
-        slot_tile[slot] = tile
-        issued.extend([tile] * LW)
+
+def protocol(cfg):
+    p = spt.gemm_pipeline_protocol(*cfg)
+    assert p is not None, f"no kernel {cfg}"
+    return p
+
+
+def test_protocol_export_matches_kernel_tables():
+    for cfg in PLAIN_KERNELS + SPLIT_KERNELS + TWO_GROUP_KERNELS:
+        bm, bn, bk, s, w = cfg
+        p = protocol(cfg)
+        issuers = 4 if w == 8 else w
+        assert p["la"] * issuers * 1024 == bm * bk * 2 and p["lb"] * issuers * 1024 == bn * bk * 2
+        assert p["split"] == (1 if (bk, s) == (64, 5) else 0)
+        assert max(p["prologue_wait"], p["handover_wait"]) < 64  # the 6-bit vmcnt field
+    assert spt.gemm_pipeline_protocol(96, 64, 64, 2, 4) is None
+
+
+def replay_ring(KT, S, p, wait_slack=0, refill_before_barrier=False):
+    """Replay the 4-wave kernel's K-loop for one wave (waves are symmetric; a barrier is a point all
+    of them reach). Loads complete in issue order; vmcnt(n) returns once at most n of this wave's
+    loads are outstanding. K-tiles past the end are zero-filling dummies (they still write LDS).
+    Checks: a K-tile is read only after all its loads landed, and a slot is refilled only after
+    every wave finished reading the K-tile it held."""
+    LW = p["lw"]
+    issued = []          # K-tile of each issued load, in order
+    slot_tile = {}       # slot -> K-tile it holds (or is receiving)
+    reads_done = set()   # K-tiles every wave has finished reading (lgkmcnt(0), then the barrier)
+    state = {"landed_upto": -1}
+
+    def issue(tile, n):
+        slot = tile % S
+        if slot_tile.get(slot) != tile:
+            prev = slot_tile.get(slot)
+            assert prev is None or prev in reads_done, f"slot {slot} refilled with K-tile {tile} before K-tile {prev} was read"
+            slot_tile[slot] = tile
+        issued.extend([tile] * n)
 
     def wait_vm(n):
-        nonlocal landed_upto
-        landed_upto = max(landed_upto, len(issued) - 1 - n)
+        state["landed_upto"] = max(state["landed_upto"], len(issued) - 1 - n)
 
     def landed(tile):
         idx = [i for i, t in enumerate(issued) if t == tile]
-        return idx and max(idx) <= landed_upto
+        return len(idx) == LW and max(idx) <= state["landed_upto"] and slot_tile[tile % S] == tile
 
-    for s in range(min(S, KT)):
-        issue(s, s)
-    wait_vm(LW * (min(KT, S) - 1))
-    assert landed(0), "tile 0 read before it landed"
-    slot = 0
+    for t in range(S):  # prologue: the first S K-tiles (dummies past the end included)
+        issue(t, LW)
+    wait_vm(p["prologue_wait"] + wait_slack)
+    assert landed(0), "K-tile 0 read before it landed"
     for k in range(KT):
-        if k + 1 < KT:
-            if refill_before_barrier and S > 1 and k + S < KT:
-                issue(slot, k + S)  # planted mistake: refill before the barrier releases the slot
-            reads_done.add(k)  # lgkmcnt(0) then the barrier: every wave finished reading tile k
-            if S == 1:
-                issue(0, k + 1)
-                wait_vm(0)
-            else:
-                ahead = min(k + S - 1, KT - 1) - (k + 1)
-                wait_vm(LW * min(ahead, S - 2) + wait_slack)
-                if k + S < KT and not refill_before_barrier:
-                    issue(slot, k + S)
-            assert landed(k + 1), f"tile {k + 1} read before it landed (KT={KT}, S={S})"
-            assert slot_tile[(k + 1) % S] == k + 1
-        else:
+        if k >= 1 and p["refill_later"]:
+            issue(k - 1 + S, p["refill_later"])  # k-step 0: the rest of the refill begun at the last hand-over
+        if k + 1 == KT:
             reads_done.add(k)
-        slot = (slot + 1) % S
-    assert sorted(set(issued)) == list(range(KT))
+            break
+        # hand-over: lgkmcnt(0), vmcnt(handover_wait), barrier, then the refill of K-tile k+S
+        if S == 1:
+            reads_done.add(k)
+            issue(k + 1, LW)
+            wait_vm(0)
+        else:
+            if refill_before_barrier:
+                issue(k + S, p["refill_now"])  # planted mistake: the refill before the barrier
+            wait_vm(p["handover_wait"] + wait_slack)
+            reads_done.add(k)
+            issue(k + S, p["refill_now"])
+        assert landed(k + 1), f"K-tile {k + 1} read before it landed (KT={KT}, S={S})"
 
 
-@pytest.mark.parametrize("S", [1, 2, 3, 4])
-def test_ring_protocol_replay(S):
-    for KT in range(1, 2 * S + 3):
-        replay_ring(KT, S, LW=4)
+@pytest.mark.parametrize("cfg", PLAIN_KERNELS)
+def test_ring_protocol_replay(cfg):
+    p = protocol(cfg)
+    S = cfg[3]
+    for KT in range(1, 2 * S + 4):
+        replay_ring(KT, S, p)
 
 
-@pytest.mark.parametrize("S", [2, 3, 4])
-def test_ring_replay_catches_planted_mistakes(S):
-    # a vmcnt threshold one load too lax lets a wave read a tile that has not fully landed
+@pytest.mark.parametrize("cfg", [c for c in PLAIN_KERNELS if c[3] >= 2])
+def test_ring_replay_catches_planted_mistakes(cfg):
+    p = protocol(cfg)
+    S = cfg[3]
+    # a vmcnt threshold one load too lax lets a wave read a K-tile that has not fully landed
     with pytest.raises(AssertionError, match="before it landed"):
-        for KT in range(1, 2 * S + 3):
-            replay_ring(KT, S, LW=4, wait_slack=1)
-    # refilling a slot before the barrier overwrites a tile other waves may still be reading
+        for KT in range(1, 2 * S + 4):
+            replay_ring(KT, S, p, wait_slack=1)
+    # refilling a slot before the barrier overwrites a K-tile other waves may still be reading
     with pytest.raises(AssertionError, match="refilled"):
-        for KT in range(1, 2 * S + 3):
-            replay_ring(KT, S, LW=4, refill_before_barrier=True)
+        for KT in range(1, 2 * S + 4):
+            replay_ring(KT, S, p, refill_before_barrier=True)
 
 
 # The split ring (five operand slots of one K-tile each): K-tile k's A tile is operand tile 2k, its B
-# tile 2k+1, and operand tile h sits in slot h mod 5. The prologue loads operand tiles 0 .. 4; k-step
-# 0 of tile k (k >= 1) loads A(k+2); at tile k's hand-over the wave waits until at most LA loads are
-# outstanding, syncs, and loads B(k+2) during the hand-over k-step. Tiles past the end are dummies.
-def replay_split_ring(KT, LA, LB, wait_slack=0, early_b=False):
+# tile 2k+1, and operand tile h sits in slot h mod 5. The prologue loads operand tiles 0 .. 4; at the
+# hand-over of K-tile k the wave waits, syncs and loads B(k+2) (refill_now loads) in the hand-over
+# k-step; k-step 0 of K-tile k+1 loads A(k+3) (refill_later loads). Tiles past the end are dummies.
+def replay_split_ring(KT, p, wait_slack=0, early_b=False):
+    LA, LB = p["la"], p["lb"]
+    assert (p["refill_now"], p["refill_later"]) == (LB, LA)
     issued = []        # operand tile of each load, in order
     slot_of = {}       # slot -> operand tile it holds
-    read = set()       # K-tiles whose fragment reads completed everywhere (lgkmcnt(0) + barrier)
-    landed_upto = -1
+    read = set()       # K-tiles whose fragment reads completed everywhere
+    state = {"landed_upto": -1}
 
     def load(h):
         slot = h % 5
         prev = slot_of.get(slot)
-        if prev is not None and prev // 2 < KT:
+        if prev is not None:
             assert prev // 2 in read, f"slot {slot} refilled with operand tile {h} before K-tile {prev // 2} was read"
         slot_of[slot] = h
         issued.extend([h] * (LA if h % 2 == 0 else LB))
 
     def wait_vm(n):
-        nonlocal landed_upto
-        landed_upto = max(landed_upto, len(issued) - 1 - n)
+        state["landed_upto"] = max(state["landed_upto"], len(issued) - 1 - n)
 
     def landed(k):
         idx = [i for i, h in enumerate(issued) if h in (2 * k, 2 * k + 1)]
-        return idx and max(idx) <= landed_upto and slot_of[(2 * k) % 5] == 2 * k and slot_of[(2 * k + 1) % 5] == 2 * k + 1
+        return (idx and max(idx) <= state["landed_upto"] and slot_of[(2 * k) % 5] == 2 * k
+                and slot_of[(2 * k + 1) % 5] == 2 * k + 1)
 
     for h in range(5):
         load(h)
-    wait_vm(2 * LA + LB)
+    wait_vm(p["prologue_wait"] + wait_slack)
     assert landed(0), "K-tile 0 read before it landed"
     for k in range(KT):
         if k >= 1:
-            load(2 * (k + 2))                 # A(k+2), k-step 0
-        if early_b and k + 1 < KT:
-            load(2 * (k + 2) + 1)             # planted mistake: B(k+2) before the hand-over barrier
-        if k + 1 < KT:
-            read.add(k)                       # hand-over: every wave's reads of tile k are done
-            wait_vm(LA + wait_slack)
-            assert landed(k + 1), f"K-tile {k + 1} read before it landed (KT={KT})"
-            if not early_b:
-                load(2 * (k + 2) + 1)         # B(k+2), hand-over k-step
-        else:
+            load(2 * (k + 2))                 # A(k+2), k-step 0 of K-tile k
+        if k + 1 == KT:
             read.add(k)
+            break
+        if early_b:
+            load(2 * (k + 2) + 1)             # planted mistake: B(k+2) before the hand-over barrier
+        wait_vm(p["handover_wait"] + wait_slack)
+        read.add(k)                           # hand-over barrier: every wave's reads of K-tile k are done
+        assert landed(k + 1), f"K-tile {k + 1} read before it landed (KT={KT})"
+        if not early_b:
+            load(2 * (k + 2) + 1)             # B(k+2), hand-over k-step
 
 
-def test_split_ring_replay():
+@pytest.mark.parametrize("cfg", SPLIT_KERNELS)
+def test_split_ring_replay(cfg):
+    p = protocol(cfg)
     for KT in range(1, 12):
-        replay_split_ring(KT, LA=8, LB=8)
-
-
-def test_split_ring_replay_catches_planted_mistakes():
+        replay_split_ring(KT, p)
     with pytest.raises(AssertionError, match="before it landed"):
         for KT in range(1, 12):
-            replay_split_ring(KT, LA=8, LB=8, wait_slack=1)
+            replay_split_ring(KT, p, wait_slack=1)
     with pytest.raises(AssertionError, match="refilled"):
         for KT in range(1, 12):
-            replay_split_ring(KT, LA=8, LB=8, early_b=True)
+            replay_split_ring(KT, p, early_b=True)
 
 
 # The two-wave-group schedule. Phases are separated by workgroup barriers; K-tile u is read by G0 in
 # phase 2u and by G1 in phase 2u+1. S = 2: G0 loads K-tile u+1 (both operand tiles) in phase 2u and
 # waits vmcnt(0) at the end of phase 2u+1. S = 5 (split): G0 loads B(u+1) in phase 2u and waits
 # vmcnt(0) at the end of phase 2u+1; G1 loads A(u+2) in phase 2u+1 and, at the end of that phase,
-# waits until at most LA of its loads are outstanding (none when it loaded nothing). The prologue
-# (G0) loads A(0), B(0) and, for S = 5, A(1), then waits for K-tile 0.
-def replay_two_groups(KT, S, LA, g1_slack=0, g0_late_wait=False):
+# waits vmcnt(pp_g1_wait) (vmcnt(0) when it loaded nothing). The prologue (G0) loads A(0), B(0) and,
+# for S = 5, A(1), then waits vmcnt(pp_g0_prologue_wait). This replays one work unit; the kernel's
+# phase stream continues into the next unit the same way (the cursors then point into it).
+def replay_two_groups(KT, S, p, g1_slack=0, g0_late_wait=False, g0_prologue_slack=0):
+    LA = p["la"]
     loads = {0: [], 1: []}       # per group: operand tile of each load, in order
     landed = {0: -1, 1: -1}
     slot_of = {}
     read_done = {}               # K-tile -> phase after which both groups finished reading it
-    n_slots = 5 if S == 5 else 2
 
     def slot(h):
         return h % 5 if S == 5 else (h // 2) % 2 * 2 + h % 2   # S = 2: stage (k mod 2), A or B half
@@ -548,12 +586,11 @@ def replay_two_groups(KT, S, LA, g1_slack=0, g0_late_wait=False):
         for h in (2 * u, 2 * u + 1):
             assert is_landed(h), f"operand tile {h} read in phase {phase} before it landed (KT={KT}, S={S})"
 
-    # prologue (G0)
     load(0, 0, -1)
     load(0, 1, -1)
     if S == 5 and KT > 1:
         load(0, 2, -1)
-        wait(0, LA)
+        wait(0, p["pp_g0_prologue_wait"] + g0_prologue_slack)
     else:
         wait(0, 0)
     for u in range(KT):
@@ -576,21 +613,25 @@ def replay_two_groups(KT, S, LA, g1_slack=0, g0_late_wait=False):
         if not g0_late_wait:
             wait(0, 0)
         if S == 5:
-            wait(1, (LA if g1_loaded else 0) + g1_slack)
-        # barrier at the end of phase 2u+1
-    return n_slots
+            wait(1, (p["pp_g1_wait"] if g1_loaded else 0) + g1_slack)
 
 
-@pytest.mark.parametrize("S", [2, 5])
-def test_two_group_schedule_replay(S):
+@pytest.mark.parametrize("cfg", TWO_GROUP_KERNELS)
+def test_two_group_schedule_replay(cfg):
+    p = protocol(cfg)
     for KT in range(1, 12):
-        replay_two_groups(KT, S, LA=8)
+        replay_two_groups(KT, cfg[3], p)
 
 
 def test_two_group_replay_catches_planted_mistakes():
+    p5 = protocol((256, 256, 64, 5, 8))
+    p2 = protocol((256, 256, 64, 2, 8))
     with pytest.raises(AssertionError, match="before it landed"):
         for KT in range(1, 12):
-            replay_two_groups(KT, 5, LA=8, g1_slack=1)
+            replay_two_groups(KT, 5, p5, g1_slack=1)
     with pytest.raises(AssertionError, match="before it landed"):
         for KT in range(1, 12):
-            replay_two_groups(KT, 2, LA=8, g0_late_wait=True)
+            replay_two_groups(KT, 5, p5, g0_prologue_slack=1)
+    with pytest.raises(AssertionError, match="before it landed"):
+        for KT in range(1, 12):
+            replay_two_groups(KT, 2, p2, g0_late_wait=True)
