@@ -33,9 +33,9 @@ PEAK_HBM_GBS = 8000.0
 DTYPE_NAME = {0: "f16", 1: "bf16", 2: "f32"}
 
 
-def load_traffic(workload: str, shape_index: int, kernel: str) -> float | None:
+def load_traffic(workload: str, shape_index: int, kernel: str, cold: bool = False) -> float | None:
     """HBM bytes per launch from the committed counter summary, if it matches these sources."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}_{shape_index}.json")
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}_{shape_index}{'_cold_b' if cold else ''}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -212,7 +212,7 @@ def main() -> int:
     achieved = flop / (avg_launch_ms * 1e-3) / 1e12
     run_config = {"plan": desc, "parts": parts}
     kernel_name = run_kernel_label(run_config, DTYPE_NAME[in_dt], DTYPE_NAME[out_dt])
-    traffic = load_traffic(args.workload, args.shape_index, kernel_name)
+    traffic = load_traffic(args.workload, args.shape_index, kernel_name, args.cold)
     compulsory = (M * K + N * K) * 2 + M * N * (4 if out_dt == 2 else 2)
     hbm_bound = compulsory / (PEAK_HBM_GBS * 1e9) > flop / (PEAK_TFLOPS * 1e12)
 
