@@ -14,6 +14,10 @@
         over the launch's duration) and the MFMA utilisation at that clock; the flop count comes
         from SQ_INSTS_VALU_MFMA_MOPS_BF16 or _F16 (512 flop each) and is checked against 2MNK
 
+    python -m software_pipelined_tiled_amd.profsum issue OUT_MD LABEL=CSV[,CSV...] ... --ktiles N --command CMD
+        where a mainloop wave's time goes, per wave and K-tile (SQ_WAVE_CYCLES split into issue, waits at
+        issue and waits on counters and barriers, with the instruction mix), one column per kernel
+
     python -m software_pipelined_tiled_amd.profsum lds COUNTER_CSV OUT_MD --command CMD
         bank-conflict ratio SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE of each LDS read-pattern probe
         launched by `python3 -m software_pipelined_tiled_amd.probes lds` (swizzles -1, 0 .. 4 in order)
@@ -296,57 +300,55 @@ def lds(counter_csv: str, out_md: str, command: str) -> None:
     print("\n".join(out))
 
 
-LIBRARY_KERNELS = (("gemm_pp_kernel", "two-group (default plan)"), ("gemm_dma_kernel", "4-wave split ring"),
-                   ("Cijk", "vendor library via torch.mm (context)"))
-COMPARE_COUNTERS = ("SQ_INSTS_LDS", "SQ_INSTS_SALU", "SQ_INSTS_VALU", "SQ_INSTS_VMEM_RD", "SQ_INSTS_VMEM_WR",
-                    "SQ_WAVES", "SQ_WAIT_ANY", "SQ_WAVE_CYCLES", "SQ_VMEM_TA_ADDR_FIFO_FULL",
-                    "SQ_LDS_BANK_CONFLICT", "FETCH_SIZE")
+# SQ counters that count quad-cycles (4 shader clocks) per wave; multiplied by 4 in the issue summary
+QUAD_CYCLE_COUNTERS = ("SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_WAIT_INST_LDS", "SQ_ACTIVE_INST_ANY",
+                       "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_SCA", "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_VMEM",
+                       "SQ_ACTIVE_INST_MISC", "SQ_INST_CYCLES_VMEM_RD")
 
 
-def compare(counter_csvs: list[str], agent_csv: str, out_md: str, command: str, flop: float) -> None:
-    """Per-kernel means of the `library` probe's counter passes: clock, MFMA utilisation, instruction mix."""
-    gpu = next(r for r in _rows(agent_csv) if r.get("Agent_Type") == "GPU")
-    n_se, n_cu = int(gpu["Num_Shader_Banks"]), int(gpu["Cu_Count"])
-    per = {}  # label -> list of per-dispatch dicts (dispatches of one pass keep their own clock)
-    for path in counter_csvs:
-        disp = {}
-        for r in _rows(path):
-            label = next((lab for key, lab in LIBRARY_KERNELS if key in r["Kernel_Name"]), None)
-            if label is None:
-                continue
-            d = disp.setdefault((label, int(r["Dispatch_Id"])),
-                                {"dur": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9})
-            d[r["Counter_Name"]] = float(r["Counter_Value"])
-        firsts = set()
-        for (label, did), d in sorted(disp.items(), key=lambda x: x[0][1]):
-            if label not in firsts:  # the first launch of each kernel in a pass warms caches and clocks
-                firsts.add(label)
-                continue
-            per.setdefault(label, []).append(d)
-    out = ["# Clock, MFMA utilisation and instruction mix on 8192^3 bf16: this library against the vendor library",
-           "", f"Command: `{command}`", "",
-           "The vendor library's GEMM (hipBLASLt, reached through torch.mm) is run for context only: it is neither",
-           "the oracle nor part of this library. Means over the launches of each kernel after its first in each",
-           f"pass. clock = SQ_BUSY_CYCLES / {n_se} shader engines / duration; MFMA utilisation = 2MNK / duration /",
-           f"({n_cu} CUs x 4096 flop/clk x clock). Instruction counts are per launch, summed over the chip.", "",
-           "| kernel | launches | duration (us) | TFLOP/s | clock (GHz) | MFMA util. at that clock | "
-           + " | ".join(COMPARE_COUNTERS) + " |",
-           "|---|---|---|---|---|---|" + "---|" * len(COMPARE_COUNTERS)]
-    for _, label in LIBRARY_KERNELS:
-        ds = per.get(label, [])
-        if not ds:
+def _gemm_counter_means(path: str) -> dict:
+    """Per-dispatch means of every counter of the GEMM mainloop kernels in one pass (the first dispatch,
+    which warms caches and clocks, left out)."""
+    disp = {}
+    for r in _rows(path):
+        if "gemm_" not in r["Kernel_Name"]:
             continue
-        clk = [d["SQ_BUSY_CYCLES"] / n_se / d["dur"] for d in ds if "SQ_BUSY_CYCLES" in d]
-        util = [flop / d["dur"] / (n_cu * 4096 * (d["SQ_BUSY_CYCLES"] / n_se / d["dur"])) for d in ds
-                if "SQ_BUSY_CYCLES" in d]
-        dur = statistics.mean(d["dur"] for d in ds)
+        d = disp.setdefault(int(r["Dispatch_Id"]), {})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    ids = sorted(disp)[1:] or sorted(disp)
+    names = set().union(*(disp[i] for i in ids)) if ids else set()
+    return {c: statistics.mean(disp[i].get(c, 0.0) for i in ids) for c in names}
+
+
+def issue(runs: list[str], out_md: str, command: str, ktiles: int) -> None:
+    """Where a mainloop wave's time goes, per wave and K-tile: one or more counter passes per kernel
+    (label=csv[,csv...]); every pass must come from the same workload, whose workgroups each run
+    `ktiles` K-tiles. Quad-cycle counters are converted to shader clocks."""
+    table = {}
+    for spec in runs:
+        label, paths = spec.split("=", 1)
+        merged = {}
+        for path in paths.split(","):
+            merged.update(_gemm_counter_means(path))
+        table[label] = merged
+    counters = sorted(set().union(*table.values()) - {"SQ_WAVES", "SQ_BUSY_CYCLES"})  # not per-wave counts
+    out = ["# Per wave and K-tile: issue, stalls and instruction mix of the GEMM mainloop kernels", "",
+           f"Command: `{command}`", "",
+           f"Means over the dispatches after the first of each pass; per wave and K-tile = counter / SQ_WAVES / "
+           f"{ktiles} K-tiles per workgroup. Counters that count quad-cycles (SQ_WAVE_CYCLES, SQ_WAIT_*, "
+           "SQ_ACTIVE_INST_*, SQ_INST_CYCLES_VMEM_RD) are multiplied by 4 to give shader clocks; the instruction "
+           "counts (SQ_INSTS_*) and SQ_VALU_MFMA_BUSY_CYCLES (clocks, per SIMD) are as counted.", "",
+           "| counter | " + " | ".join(table) + " |", "|---|" + "---|" * len(table)]
+    for c in counters:
         cells = []
-        for c in COMPARE_COUNTERS:
-            v = [d[c] for d in ds if c in d]
-            cells.append(f"{statistics.mean(v):.4g}" if v else "")
-        out.append(f"| {label} | {len(ds)} | {dur * 1e6:.1f} | {flop / dur / 1e12:.1f} | "
-                   f"{statistics.mean(clk) / 1e9 if clk else float('nan'):.3f} | "
-                   f"{statistics.mean(util) if util else float('nan'):.3f} | " + " | ".join(cells) + " |")
+        for label, m in table.items():
+            waves = m.get("SQ_WAVES", 0.0)
+            if c not in m or waves <= 0:
+                cells.append("")
+                continue
+            v = m[c] / waves / ktiles * (4 if c in QUAD_CYCLE_COUNTERS else 1)
+            cells.append(f"{v:.1f}")
+        out.append(f"| {c} | " + " | ".join(cells) + " |")
     with open(out_md, "w") as f:
         f.write("\n".join(out) + "\n")
     print("\n".join(out))
@@ -367,12 +369,13 @@ def main(argv=None) -> int:
     d = sub.add_parser("lds")
     d.add_argument("counter_csv"), d.add_argument("out_md")
     d.add_argument("--command", required=True)
-    cp = sub.add_parser("compare")
-    cp.add_argument("agent_csv"), cp.add_argument("out_md"), cp.add_argument("counter_csvs", nargs="+")
-    cp.add_argument("--command", required=True)
+    iss = sub.add_parser("issue")
+    iss.add_argument("out_md"), iss.add_argument("runs", nargs="+", help="label=csv[,csv...] per kernel")
+    iss.add_argument("--ktiles", type=int, required=True, help="K-tiles each workgroup runs")
+    iss.add_argument("--command", required=True)
     a = ap.parse_args(argv)
-    if a.what == "compare":
-        compare(a.counter_csvs, a.agent_csv, a.out_md, a.command, 2.0 * 8192 ** 3)
+    if a.what == "issue":
+        issue(a.runs, a.out_md, a.command, a.ktiles)
     elif a.what == "lds":
         lds(a.counter_csv, a.out_md, a.command)
     elif a.what == "clock":
