@@ -93,6 +93,13 @@ typedef enum {
  *                partial plane; a second kernel adds the planes in range order and rounds once.
  *                The built-in choice splits when the output tiles alone leave workgroup slots of
  *                the device idle. DMA and staged paths only
+ *   stream       cache hint for an operand that only one workgroup reads: 0 none, 1 A, 2 B. The
+ *                hinted operand is loaded non-temporally (streaming replacement, not kept in L2
+ *                or the MALL for a later launch), which leaves the cache to the shared operand.
+ *                Only the 32x32 tiles (bk 128, waves 2) have these variants; others with a
+ *                nonzero value are GEMM_ERR_UNSUPPORTED. The built-in choice streams B when all
+ *                of M fits one tile row and B spans at least 64 MiB (A likewise when N fits one
+ *                tile column), with the 8-deep ring. Results are identical with and without it
  */
 typedef struct {
   int bm, bn, bk;
@@ -105,6 +112,7 @@ typedef struct {
   int grid;
   int lds_bytes;
   int splits;
+  int stream;
 } gemm_config_t;
 
 typedef struct gemm_plan_s* gemm_plan_t;

@@ -35,7 +35,7 @@ class GemmError(RuntimeError):
 
 class GemmConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in ("bm", "bn", "bk", "stages", "waves", "mfma", "persistent", "group_m",
-                                            "load_path", "grid", "lds_bytes", "splits")]
+                                            "load_path", "grid", "lds_bytes", "splits", "stream")]
 
     def as_dict(self) -> dict:
         return {n: getattr(self, n) for n, _ in self._fields_}

@@ -62,6 +62,13 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* lds, unsig
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, voffset, soffset, 0, 0);
 }
 
+// The same load with the non-temporal hint (the nt bit of the instruction's cache policy): the
+// lines take the streaming replacement policy and are not kept for reuse, for an operand every
+// byte of which one workgroup reads once, so that it does not displace the operand the others share.
+__device__ __forceinline__ void dma16_stream(__amdgpu_buffer_rsrc_t r, void* lds, unsigned voffset, unsigned soffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, voffset, soffset, 0, 2);
+}
+
 // LDS byte address of a pointer into a __shared__ array.
 __device__ __forceinline__ unsigned lds_addr(const void* p) { return (unsigned)(uintptr_t)(const lds_void_t*)p; }
 

@@ -28,7 +28,7 @@ struct Regions {
   int a, b;  // LDS byte offsets of a K-tile's A and B tiles
 };
 
-template <int BM, int BN, int BK, int S, int WM, int WN, typename TIn, int OUT>
+template <int BM, int BN, int BK, int S, int WM, int WN, typename TIn, int OUT, int STREAM>
 __global__ void __launch_bounds__(WM* WN * 64, 1) gemm_dma_kernel(GemmArgs args) {
   using T = TileShape<BM, BN, BK, S, WM, WN>;
   // 16 bytes past the ring hold the dynamic schedule's next unit, where the ring leaves room for them
@@ -145,12 +145,14 @@ __global__ void __launch_bounds__(WM* WN * 64, 1) gemm_dma_kernel(GemmArgs args)
       if (d < T::LA) {
         const int g = (wave * T::LA + d) / (BM / T::RPI);
         char* sa = smem + dst.a + (wave * T::LA + d) * 1024;
-        dma16(ra, sa, lane_kc < K - k0 - T::GK * g ? a_off[d] : kOOB, 2u * k0);
+        if constexpr (STREAM == 1) dma16_stream(ra, sa, lane_kc < K - k0 - T::GK * g ? a_off[d] : kOOB, 2u * k0);
+        else dma16(ra, sa, lane_kc < K - k0 - T::GK * g ? a_off[d] : kOOB, 2u * k0);
       } else {
         const int j = d - T::LA;
         const int g = (wave * T::LB + j) / (BN / T::RPI);
         char* sb = smem + dst.b + (wave * T::LB + j) * 1024;
-        dma16(rb, sb, lane_kc < K - k0 - T::GK * g ? b_off[j] : kOOB, 2u * k0);
+        if constexpr (STREAM == 2) dma16_stream(rb, sb, lane_kc < K - k0 - T::GK * g ? b_off[j] : kOOB, 2u * k0);
+        else dma16(rb, sb, lane_kc < K - k0 - T::GK * g ? b_off[j] : kOOB, 2u * k0);
       }
     };
     auto issue = [&](Regions dst, int kt) {
@@ -382,19 +384,30 @@ __global__ void __launch_bounds__(WM* WN * 64, 1) gemm_dma_kernel(GemmArgs args)
 }
 
 // ------------------------------------------------------------------------------ instantiation table
-template <int BM, int BN, int BK, int S, int WM, int WN>
+template <int BM, int BN, int BK, int S, int WM, int WN, int STREAM>
+static void fill_fns(const void* (&fn)[2][3]) {
+  fn[0][0] = (const void*)&gemm_dma_kernel<BM, BN, BK, S, WM, WN, _Float16, 0, STREAM>;
+  fn[0][1] = (const void*)&gemm_dma_kernel<BM, BN, BK, S, WM, WN, _Float16, 1, STREAM>;
+  fn[0][2] = (const void*)&gemm_dma_kernel<BM, BN, BK, S, WM, WN, _Float16, 2, STREAM>;
+  fn[1][0] = (const void*)&gemm_dma_kernel<BM, BN, BK, S, WM, WN, __bf16, 0, STREAM>;
+  fn[1][1] = (const void*)&gemm_dma_kernel<BM, BN, BK, S, WM, WN, __bf16, 1, STREAM>;
+  fn[1][2] = (const void*)&gemm_dma_kernel<BM, BN, BK, S, WM, WN, __bf16, 2, STREAM>;
+}
+
+// HINTS: also instantiate the variants that load A (fn_stream[0]) or B (fn_stream[1]) with the
+// non-temporal hint
+template <int BM, int BN, int BK, int S, int WM, int WN, bool HINTS = false>
 static KernelEntry make_entry() {
   using T = TileShape<BM, BN, BK, S, WM, WN>;
   KernelEntry e;
   e.bm = BM; e.bn = BN; e.bk = BK; e.stages = S; e.waves = T::W; e.load_path = 1;
   e.lds_bytes = T::LDS;
   e.mfma = 16;
-  e.fn[0][0] = (const void*)&gemm_dma_kernel<BM, BN, BK, S, WM, WN, _Float16, 0>;
-  e.fn[0][1] = (const void*)&gemm_dma_kernel<BM, BN, BK, S, WM, WN, _Float16, 1>;
-  e.fn[0][2] = (const void*)&gemm_dma_kernel<BM, BN, BK, S, WM, WN, _Float16, 2>;
-  e.fn[1][0] = (const void*)&gemm_dma_kernel<BM, BN, BK, S, WM, WN, __bf16, 0>;
-  e.fn[1][1] = (const void*)&gemm_dma_kernel<BM, BN, BK, S, WM, WN, __bf16, 1>;
-  e.fn[1][2] = (const void*)&gemm_dma_kernel<BM, BN, BK, S, WM, WN, __bf16, 2>;
+  fill_fns<BM, BN, BK, S, WM, WN, 0>(e.fn);
+  if constexpr (HINTS) {
+    fill_fns<BM, BN, BK, S, WM, WN, 1>(e.fn_stream[0]);
+    fill_fns<BM, BN, BK, S, WM, WN, 2>(e.fn_stream[1]);
+  }
   return e;
 }
 
@@ -415,9 +428,10 @@ const KernelEntry* dma_kernel_table(int* count) {
       make_entry<64, 64, 128, 4, 2, 2>(),
       make_entry<64, 64, 64, 2, 2, 2>(),
       // skinny shapes (M of a few dozen rows): a 32x32 tile with 128-deep K-tiles and two waves keeps
-      // one workgroup per 32 columns streaming, with up to seven 8 KiB operand tiles of B in flight
-      make_entry<32, 32, 128, 4, 2, 1>(),
-      make_entry<32, 32, 128, 8, 2, 1>(),
+      // one workgroup per 32 columns streaming, with up to seven 8 KiB operand tiles of B in flight;
+      // the operand only one workgroup reads can be streamed with the non-temporal hint
+      make_entry<32, 32, 128, 4, 2, 1, true>(),
+      make_entry<32, 32, 128, 8, 2, 1, true>(),
   };
   *count = (int)(sizeof(table) / sizeof(table[0]));
   return table;

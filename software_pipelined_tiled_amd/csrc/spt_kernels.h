@@ -8,6 +8,8 @@ struct KernelEntry {
   int lds_bytes;
   int mfma;  // 16: v_mfma_f32_16x16x32, 32: v_mfma_f32_32x32x16
   const void* fn[2][3];  // __global__ void(GemmArgs), by [input f16/bf16][output f16/bf16/f32]
+  // the same kernels loading A ([0]) or B ([1]) with the non-temporal hint; null where not built
+  const void* fn_stream[2][2][3] = {};
 };
 
 const KernelEntry* dma_kernel_table(int* count);

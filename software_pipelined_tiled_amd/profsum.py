@@ -105,6 +105,7 @@ def kernel_label(plan: dict, in_dt: str, out_dt: str) -> str:
     extra = f",splits={splits}" if splits > 1 else ""
     extra += ",staged" if plan["load_path"] == 3 else ""
     extra += ",mfma32x32x16" if plan.get("mfma", 16) == 32 else ""
+    extra += {1: ",stream=A", 2: ",stream=B"}.get(plan.get("stream", 0), "")
     return (f"gemm_{kind}_kernel<{plan['bm']},{plan['bn']},{plan['bk']},{plan['stages']},"
             f"waves={plan['waves']},{in_dt},{out}{extra}>")
 

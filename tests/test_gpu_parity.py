@@ -36,9 +36,10 @@ REG_CONFIGS = [(128, 128, 2), (64, 64, 2), (128, 128, 1)]
 RING_CONFIGS = [(64, 5, 4), (32, 4, 4), (64, 5, 8), (64, 2, 8)]
 
 
-def cfg(bm, bn, s, path=spt.GEMM_LOAD_DMA, persistent=1, group_m=8, grid=0, bk=64, waves=4, splits=1, mfma=16):
+def cfg(bm, bn, s, path=spt.GEMM_LOAD_DMA, persistent=1, group_m=8, grid=0, bk=64, waves=4, splits=1, mfma=16,
+        stream=0):
     return dict(bm=bm, bn=bn, bk=bk, stages=s, waves=waves, mfma=mfma, persistent=persistent, group_m=group_m,
-                load_path=path, grid=grid, lds_bytes=0, splits=splits)
+                load_path=path, grid=grid, lds_bytes=0, splits=splits, stream=stream)
 
 
 def ring_cfg(bk, s, waves, **kw):
@@ -164,6 +165,36 @@ def test_skinny_32_tile_bit_exact(K, s, persistent, splits):
                                      grid=2 if persistent else 0))
         assert (desc["bm"], desc["bn"], desc["bk"], desc["stages"], desc["waves"]) == (32, 32, 128, s, 2)
         check_full(a, b, K, si.F16, si.F32, c, N, exact=True)
+
+
+@pytest.mark.parametrize("K", [136, 1032, 1024 + 8 * 128 + 40])
+@pytest.mark.parametrize("s", [4, 8])
+@pytest.mark.parametrize("persistent,splits", [(1, 1), (0, 1), (1, 3)])
+@pytest.mark.parametrize("stream", [1, 2])
+def test_stream_hint_bit_exact(K, s, persistent, splits, stream):
+    # the non-temporal hint on A or on B changes where lines are cached, not what is computed:
+    # every output equals the oracle's exactly, on the staged path too (K not a multiple of 8)
+    for M, N in ((32, 5 * 32 - 9), (2 * 32 + 13, 2 * 32 - 5)):
+        for k in (K, K - 3):
+            a = ints(M, k, si.F16, 70 + k + M + s)
+            b = ints(N, k, si.F16, 71 + k + N + s)
+            path = spt.GEMM_LOAD_DMA if k % 8 == 0 else spt.GEMM_LOAD_STAGED
+            c, desc = run_gpu(a, b, k, si.F16, si.F32,
+                              config=cfg(32, 32, s, bk=128, waves=2, persistent=persistent, splits=splits,
+                                         grid=2 if persistent else 0, stream=stream, path=path))
+            assert (desc["bm"], desc["stages"], desc["stream"], desc["load_path"]) == (32, s, stream, path)
+            check_full(a, b, k, si.F16, si.F32, c, N, exact=True)
+
+
+def test_stream_hint_auto_on_a():
+    # the transpose of the skinny shape: N = 32 columns, so every A tile is read by one workgroup and
+    # the built-in plan streams A (128 MiB) with the hint; every output against the oracle
+    M, N, K = 8192, 32, 8192
+    a = si.make_matrix(M, K, si.F16, "uniform", 0x5A11, ld=K)
+    b = si.make_matrix(N, K, si.F16, "uniform", 0x5A12, ld=K)
+    c, desc = run_gpu(a, b, K, si.F16, si.F16)
+    assert (desc["bm"], desc["bn"], desc["stages"], desc["stream"]) == (32, 32, 8, 1)
+    check_full_blocked(a, b, K, si.F16, si.F16, c, N)
 
 
 @pytest.mark.parametrize("bm,bn,s", REG_CONFIGS)

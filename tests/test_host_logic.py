@@ -116,8 +116,31 @@ def test_config_choice(name):
         # M = 32: a larger tile would be mostly padding. The time is B streaming in at the HBM rate;
         # 256 workgroups of 32x32 tiles with 128-deep K-tiles stream it (one per 32 columns), so K
         # stays whole and no partial planes are written and reduced
-        assert (c["bm"], c["bn"], c["bk"], c["stages"], c["waves"]) == (32, 32, 128, 4, 2) and c["splits"] == 1
-        assert c["grid"] == 256
+        # B (128 MiB, each tile read by one workgroup) streams with the non-temporal hint through the
+        # 8-deep ring
+        assert (c["bm"], c["bn"], c["bk"], c["stages"], c["waves"]) == (32, 32, 128, 8, 2) and c["splits"] == 1
+        assert c["grid"] == 256 and c["stream"] == 2
+    else:
+        assert c["stream"] == 0
+
+
+@pytest.mark.parametrize("M,N,K,tile,stream", [
+    (32, 8192, 8192, (32, 32, 128, 8, 2), 2),     # B, 128 MiB, read once: streamed
+    (8192, 32, 8192, (32, 32, 128, 8, 2), 1),     # the transpose: A streamed
+    (17, 16384, 4096, (32, 32, 128, 8, 2), 2),    # a ragged single tile row, B exactly 128 MiB
+    (32, 2048, 8192, (32, 32, 128, 4, 2), 0),     # B of 32 MiB: below the 64 MiB floor, no hint
+    (64, 8192, 8192, None, 0),                    # two tile rows of 32 share B: no hint
+])
+def test_stream_hint_rule(M, N, K, tile, stream):
+    c = spt.gemm_select_config(M, N, K, F16, F16, F16, K, K, N, 256, 160 * 1024)
+    if tile is not None:
+        assert (c["bm"], c["bn"], c["bk"], c["stages"], c["waves"]) == tile
+    assert c["stream"] == stream
+    assert c["lds_bytes"] == ring_bytes(c)
+    if stream == 2:
+        assert M <= c["bm"] and 2 * N * K >= 64 << 20
+    if stream == 1:
+        assert N <= c["bn"] and 2 * M * K >= 64 << 20
 
 
 def test_staging_needs_each_source_under_2gib():
@@ -200,6 +223,11 @@ GOOD_OVERRIDE = dict(bm=128, bn=128, bk=64, stages=4, waves=4, mfma=16, persiste
     ((256, 256, 256), dict(bm=256, bn=256, stages=5, waves=8, persistent=2), UNSUPPORTED),  # no queue in two-group
     ((256, 256, 256), dict(bm=256, bn=256, stages=5, persistent=2), UNSUPPORTED),  # ring leaves no queue slot
     ((16384, 16384, 1024), dict(splits=2), UNSUPPORTED),                      # partial planes above 1 GiB
+    ((256, 256, 256), dict(stream=3), INVALID),
+    ((256, 256, 256), dict(stream=-1), INVALID),
+    ((256, 256, 256), dict(stream=2), UNSUPPORTED),                           # 128x128 has no hinted variant
+    ((32, 256, 256), dict(bm=32, bn=32, bk=128, stages=4, waves=2, load_path=2, stream=2), INVALID),  # no REG 32x32
+    ((256, 256, 256), dict(load_path=2, stages=2, stream=1), UNSUPPORTED),    # register path: no hint
 ])
 def test_config_override_validation(shape, change, status):
     # every rejected override returns its own status from the host-only selection and from plan
@@ -223,6 +251,11 @@ def test_config_override_accepted_and_reported():
     c = spt.gemm_select_config(1000, 700, 512, BF16, BF16, F32, 512, 512, 700, cu_count=32,
                                config=dict(GOOD_OVERRIDE, splits=3))
     assert c["grid"] == 32 and c["splits"] == 3
+    # the streaming hint on request, on the 32x32 tiles, for either operand
+    for st in (1, 2):
+        c = spt.gemm_select_config(4000, 700, 512, F16, F16, F16, 512, 512, 700, config=dict(
+            GOOD_OVERRIDE, bm=32, bn=32, bk=128, stages=8, waves=2, stream=st))
+        assert c["stream"] == st and (c["bm"], c["stages"]) == (32, 8)
     # the staged path on request, where DMA cannot read the rows directly
     c = spt.gemm_select_config(100, 70, 77, F16, F16, F16, 77, 77, 70, config=dict(GOOD_OVERRIDE, load_path=3))
     assert c["load_path"] == spt.GEMM_LOAD_STAGED
