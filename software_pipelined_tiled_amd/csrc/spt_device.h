@@ -155,13 +155,18 @@ __device__ __forceinline__ f32x16 mfma32<_Float16>(u32x4 x, u32x4 y, f32x16 c) {
 }
 
 // ------------------------------------------------------------------------------ epilogue
+// Two fp32 values rounded to nearest-even and packed, a in the low half. Converting them as one
+// two-element vector gives gfx950's two-source conversions (v_cvt_pk_bf16_f32 and v_cvt_pk_f16_f32,
+// one instruction per pair); two scalar conversions cost a conversion per value plus a shift and an
+// or per pair, four times the VALU work of an output tile's epilogue.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ unsigned pack_bf16(float a, float b) {
-  return (unsigned)__builtin_bit_cast(unsigned short, (__bf16)a) |
-         ((unsigned)__builtin_bit_cast(unsigned short, (__bf16)b) << 16);
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 __device__ __forceinline__ unsigned pack_f16(float a, float b) {
-  return (unsigned)__builtin_bit_cast(unsigned short, (_Float16)a) |
-         ((unsigned)__builtin_bit_cast(unsigned short, (_Float16)b) << 16);
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{a, b}, f16x2));
 }
 
 // Store the 8 consecutive outputs v[0..7] at row m_rel (relative to the tile's first row),

@@ -211,14 +211,49 @@ def test_reg_configs_bit_exact(bm, bn, s):
 @pytest.mark.parametrize("out_dt", [si.F16, si.BF16, si.F32])
 @pytest.mark.parametrize("in_dt", [si.F16, si.BF16])
 def test_output_dtypes_bit_exact(in_dt, out_dt):
-    # integer sums up to 9·K = 2880 are exact in every output type except bf16 (8 bits), where
-    # the oracle's single rounding of the exact sum must be reproduced exactly as well
+    # integer sums up to 9·K = 2880: exact in f32; in f16 above 2048 and in bf16 above 256 they
+    # round, and the oracle's single rounding of the exact sum must be reproduced exactly
     M, N, K = 300, 264, 320
     a = ints(M, K, in_dt, 7)
     b = ints(N, K, in_dt, 8)
     for c_cfg in (cfg(256, 256, 2), cfg(128, 128, 4), cfg(128, 128, 2, path=spt.GEMM_LOAD_REG),
                   ring_cfg(64, 5, 8), ring_cfg(64, 5, 4), ring_cfg(64, 5, 8, splits=3), cfg(64, 64, 4, splits=2),
                   ring_cfg(64, 5, 8, mfma=32)):
+        c, _ = run_gpu(a, b, K, in_dt, out_dt, config=c_cfg)
+        check_full(a, b, K, in_dt, out_dt, c, N, exact=True)
+
+
+def wide_range_column(rows, K, dtype, seed, emin, emax):
+    """[rows, K] bits: column 0 normal values of random sign, exponent field in [emin, emax] and
+    random mantissa; every other column zero. A·Bᵀ of two such operands is one product per output,
+    exact in fp32, so each output tests the conversion of an fp32 value to the output type."""
+    rng = np.random.default_rng(seed)
+    mbits = 10 if dtype == si.F16 else 7
+    e = rng.integers(emin, emax + 1, rows).astype(np.uint32)
+    m = rng.integers(0, 1 << mbits, rows).astype(np.uint32)
+    sg = rng.integers(0, 2, rows).astype(np.uint32)
+    out = np.zeros((rows, K), np.uint16)
+    out[:, 0] = ((sg << 15) | (e << mbits) | m).astype(np.uint16)
+    return out
+
+
+OUTPUT_PATH_CONFIGS = (cfg(256, 256, 2), cfg(128, 128, 4), cfg(128, 128, 2, path=spt.GEMM_LOAD_REG),
+                       ring_cfg(64, 5, 8), ring_cfg(64, 5, 4), ring_cfg(64, 5, 8, splits=3),
+                       cfg(64, 64, 4, splits=2), ring_cfg(64, 5, 8, mfma=32), cfg(32, 32, 8, bk=128, waves=2, stream=2))
+
+
+@pytest.mark.parametrize("out_dt", [si.F16, si.BF16, si.F32])
+@pytest.mark.parametrize("in_dt", [si.F16, si.BF16])
+def test_output_rounding_bit_exact(in_dt, out_dt):
+    # products spanning far more than the output's range: f16 outputs overflow to infinity, fall to
+    # subnormals and to signed zero; bf16 outputs round 16-bit products to 8 bits, ties included.
+    # Every kernel's epilogue (and the split-K reduction) converts each exact fp32 product exactly as
+    # the oracle rounds it
+    M, N, K = 300, 264, 8
+    lo, hi = (1, 30) if in_dt == si.F16 else (127 - 20, 127 + 20)
+    a = wide_range_column(M, K, in_dt, 11, lo, hi)
+    b = wide_range_column(N, K, in_dt, 12, lo, hi)
+    for c_cfg in OUTPUT_PATH_CONFIGS:
         c, _ = run_gpu(a, b, K, in_dt, out_dt, config=c_cfg)
         check_full(a, b, K, in_dt, out_dt, c, N, exact=True)
 
