@@ -275,16 +275,19 @@ gemm_config_t choose(int64_t M, int64_t N, int64_t K, const Candidate* menu, int
   return best;
 }
 
-// Relative MFMA rate of a menu configuration (0.2 for one not on the menus).
+// Relative MFMA rate of a configuration: its menu entry's, else that of the same tile at another ring
+// depth (the streaming hint deepens the 32x32 ring), else 0.2.
 double rate_of(const gemm_config_t& c) {
   const bool reg = c.load_path == GEMM_LOAD_REG;
   const Candidate* menu = reg ? kRegMenu : kDmaMenu;
   const int n = reg ? kRegMenuSize : kDmaMenuSize;
-  for (int i = 0; i < n; ++i)
-    if (menu[i].bm == c.bm && menu[i].bn == c.bn && menu[i].bk == c.bk && menu[i].stages == c.stages &&
-        menu[i].waves == c.waves)
-      return menu[i].rate;
-  return 0.2;
+  double same_tile = 0.0;
+  for (int i = 0; i < n; ++i) {
+    if (menu[i].bm != c.bm || menu[i].bn != c.bn || menu[i].bk != c.bk || menu[i].waves != c.waves) continue;
+    if (menu[i].stages == c.stages) return menu[i].rate;
+    if (same_tile == 0.0) same_tile = menu[i].rate;
+  }
+  return same_tile > 0.0 ? same_tile : 0.2;
 }
 
 // The single configuration `choose` picks and its modelled time.
