@@ -84,3 +84,45 @@ def test_noalloc_rejects_workspace_beyond_scratch_and_bad_args():
     assert lib.gemm_run_noalloc(0, 8, 8, si.F16, si.F16, si.F16, 8, 8, 8, None, None, None, None) == spt._lib.GEMM_OK
     assert lib.gemm_run_noalloc(8, 8, 8, si.F16, si.F16, si.F16, 8, 8, 8, None, None, None, None) == \
         spt._lib.GEMM_ERR_INVALID
+
+
+@pytest.mark.parametrize("shape,other,in_dt,out_dt", [
+    ((700, 900, 1533), (300, 260, 999), si.F16, si.F16),        # staging copy into the scratch array
+    ((512, 768, 16384), (256, 256, 8192), si.BF16, si.F32),     # split-K partial planes in the scratch array
+])
+def test_noalloc_graph_replay_with_scratch_reused(shape, other, in_dt, out_dt):
+    # the callers this entry point is for include work recorded under graph capture. Capture one call,
+    # then replay it three times; between replays, eager calls of another shape overwrite the scratch
+    # array. Every launch writes the scratch it reads before reading it, so each replay must equal the
+    # eager result bit for bit.
+    M, N, K = shape
+    a = si.make_matrix(M, K, in_dt, "small_int", 77 + K)
+    b = si.make_matrix(N, K, in_dt, "small_int", 78 + K)
+    A, B = to_device(a, in_dt), to_device(b, in_dt)
+    odt = TORCH_DT[out_dt]
+    Mo, No, Ko = other
+    ao = to_device(si.make_matrix(Mo, Ko, in_dt, "small_int", 79 + Ko), in_dt)
+    bo = to_device(si.make_matrix(No, Ko, in_dt, "small_int", 80 + Ko), in_dt)
+    Co = torch.empty((Mo, No), dtype=odt, device="cuda")
+    C_eager = torch.full((M, N), float("nan"), dtype=odt, device="cuda")
+    C_graph = torch.full((M, N), float("nan"), dtype=odt, device="cuda")
+
+    def call(Ap, Bp, Cp, m, n, k, stream):
+        spt.gemm_run_noalloc(m, n, k, in_dt, in_dt, out_dt, k, k, n, Ap, Bp, Cp, stream)
+
+    s = torch.cuda.current_stream().cuda_stream
+    call(A.data_ptr(), B.data_ptr(), C_eager.data_ptr(), M, N, K, s)  # eager, and the device's scratch set up
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(A.data_ptr(), B.data_ptr(), C_graph.data_ptr(), M, N, K, torch.cuda.current_stream().cuda_stream)
+    want = bits(C_eager, out_dt)
+    view = np.uint32 if out_dt == si.F32 else np.uint16
+    for rep in range(3):
+        call(ao.data_ptr(), bo.data_ptr(), Co.data_ptr(), Mo, No, Ko, s)  # another shape through the scratch
+        C_graph.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(C_graph, out_dt).view(view), want.view(view)), f"replay {rep}"
+    check_full(a, b, K, in_dt, out_dt, want, N, exact=True)
