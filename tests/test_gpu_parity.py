@@ -197,6 +197,18 @@ def test_stream_hint_auto_on_a():
     check_full_blocked(a, b, K, si.F16, si.F16, c, N)
 
 
+@pytest.mark.parametrize("M,N,in_dt,stream", [(32, 8192, si.F16, 2), (8192, 32, si.BF16, 1)])
+def test_stream_hint_staged_full(M, N, in_dt, stream):
+    # K odd: rows of 8191 elements are copied into rows of 8192 first, then the built-in plan streams
+    # the copy of the large operand with the hint through the 8-deep 32x32 ring; every output
+    K = 8191
+    a = si.make_matrix(M, K, in_dt, "uniform", 0x57A6 + M)
+    b = si.make_matrix(N, K, in_dt, "uniform", 0x57A7 + N)
+    c, desc = run_gpu(a, b, K, in_dt, in_dt)
+    assert (desc["bm"], desc["stages"], desc["load_path"], desc["stream"]) == (32, 8, spt.GEMM_LOAD_STAGED, stream)
+    check_full_blocked(a, b, K, in_dt, in_dt, c, N)
+
+
 @pytest.mark.parametrize("bm,bn,s", REG_CONFIGS)
 def test_reg_configs_bit_exact(bm, bn, s):
     M, N, K = 2 * bm + 7, bn + 9, 3 * 64 + 13  # K not a multiple of 8: element-masked tail

@@ -130,6 +130,7 @@ def test_config_choice(name):
     (17, 16384, 4096, (32, 32, 128, 8, 2), 2),    # a ragged single tile row, B exactly 128 MiB
     (32, 2048, 8192, (32, 32, 128, 4, 2), 0),     # B of 32 MiB: below the 64 MiB floor, no hint
     (64, 8192, 8192, None, 0),                    # two tile rows of 32 share B: no hint
+    (32, 8192, 8191, (32, 32, 128, 8, 2), 2),     # K odd: the staged copy of B is streamed
 ])
 def test_stream_hint_rule(M, N, K, tile, stream):
     c = spt.gemm_select_config(M, N, K, F16, F16, F16, K, K, N, 256, 160 * 1024)
