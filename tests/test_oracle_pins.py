@@ -52,7 +52,8 @@ def pin_f16_encode_vs_numpy():
         [0.0, -0.0, np.inf, -np.inf],
     ])
     got = orc.encode(F16, x)
-    ref = x.astype(np.float16).view(np.uint16)
+    with np.errstate(over="ignore"):  # values past the f16 range round to infinity, as the encoder must
+        ref = x.astype(np.float16).view(np.uint16)
     assert np.array_equal(got, ref), np.nonzero(got != ref)[0][:5]
 
 
@@ -101,7 +102,8 @@ def pin_generic_encoder_vs_c_float_cast():
         RNG.standard_normal(50_000) * 1e3,
         np.ldexp(RNG.uniform(1, 2, 50_000), RNG.integers(-160, 130, 50_000)),
     ])
-    ref = x.astype(np.float32).view(np.uint32)
+    with np.errstate(over="ignore"):  # values past the f32 range round to infinity, as the encoder must
+        ref = x.astype(np.float32).view(np.uint32)
     got = np.array([lib.oracle_encode_f32_generic(float(v)) for v in x], dtype=np.uint32)
     assert np.array_equal(got, ref), np.nonzero(got != ref)[0][:5]
     f32 = orc.encode(F32, x)
@@ -182,8 +184,9 @@ def pin_small_integer_exact():
         M, N, K = 13, 17, 70
         a = si.make_matrix(M, K, dtype, "small_int", 1)
         b = si.make_matrix(N, K, dtype, "small_int", 2)
-        ai = orc.decode(dtype, a).astype(np.int64)
-        bi = orc.decode(dtype, b).astype(np.int64)
+        with np.errstate(invalid="ignore"):  # a planted decoding mistake may give NaN; the pin then fails
+            ai = orc.decode(dtype, a).astype(np.int64)
+            bi = orc.decode(dtype, b).astype(np.int64)
         c, s, t = orc.gemm(a, b, K, dtype, F32)
         assert np.array_equal(s, (ai @ bi.T).astype(np.float64))
         assert np.array_equal(t, (np.abs(ai) @ np.abs(bi).T).astype(np.float64))
