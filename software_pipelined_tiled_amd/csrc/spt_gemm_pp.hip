@@ -324,41 +324,49 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmArgs args) {
     // lines (non-temporal, 16384^2 x 1024 ran 30 % slower).
     const bool nt = MF == 16 && args.splits == 1;
     const unsigned voff = (unsigned)(m_lane * args.ldc + n_lane) * (unsigned)es;
-    // 8 consecutive outputs at (m_lane + dm, n_lane + dn)
-    auto put8 = [&](const float (&vv)[8], int dm, int dn) SPT_INLINE {
-      if (full && nt) store8_at<OUT, kStoreNonTemporal>(vv, rc, voff, (unsigned)((dm * args.ldc + dn) * es));
-      else if (full) store8_at<OUT>(vv, rc, voff, (unsigned)((dm * args.ldc + dn) * es));
-      else store8<OUT, true>(vv, rc, m_lane + dm, tl.rows_left, n_lane + dn, N, args.ldc);
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    if constexpr (MF == 16) {
-      // one store per A block and row e: columns 8c .. 8c+7 come from the FN = 8 B fragments
-#pragma unroll
-      for (int j = 0; j < FM; ++j) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float vv[8];
-#pragma unroll
-          for (int f = 0; f < FN; ++f) vv[f] = acc[f][j][e];
-          put8(vv, 16 * j + e, 0);
-        }
-      }
-    } else {
-      // elements 8h .. 8h+7 of a block hold columns 32i + 16h + 8(l/32) + 0..7
-#pragma unroll
-      for (int i = 0; i < FN; ++i) {
+    // The tile's stores in one of three forms, chosen once per tile rather than at every store:
+    // 0 interior, non-temporal; 1 interior, default policy; 2 edge tile, masked per element.
+    auto stores = [&](auto mode_c) SPT_INLINE {
+      constexpr int kMode = decltype(mode_c)::value;
+      // 8 consecutive outputs at (m_lane + dm, n_lane + dn)
+      auto put8 = [&](const float (&vv)[8], int dm, int dn) SPT_INLINE {
+        if constexpr (kMode == 0) store8_at<OUT, kStoreNonTemporal>(vv, rc, voff, (unsigned)((dm * args.ldc + dn) * es));
+        else if constexpr (kMode == 1) store8_at<OUT>(vv, rc, voff, (unsigned)((dm * args.ldc + dn) * es));
+        else store8<OUT, true>(vv, rc, m_lane + dm, tl.rows_left, n_lane + dn, N, args.ldc);
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      if constexpr (MF == 16) {
+        // one store per A block and row e: columns 8c .. 8c+7 come from the FN = 8 B fragments
 #pragma unroll
         for (int j = 0; j < FM; ++j) {
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
+          for (int e = 0; e < 4; ++e) {
             float vv[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) vv[e] = acc[i][j][8 * h + e];
-            put8(vv, 32 * j, 32 * i + 16 * h);
+            for (int f = 0; f < FN; ++f) vv[f] = acc[f][j][e];
+            put8(vv, 16 * j + e, 0);
+          }
+        }
+      } else {
+        // elements 8h .. 8h+7 of a block hold columns 32i + 16h + 8(l/32) + 0..7
+#pragma unroll
+        for (int i = 0; i < FN; ++i) {
+#pragma unroll
+          for (int j = 0; j < FM; ++j) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              float vv[8];
+#pragma unroll
+              for (int e = 0; e < 8; ++e) vv[e] = acc[i][j][8 * h + e];
+              put8(vv, 32 * j, 32 * i + 16 * h);
+            }
           }
         }
       }
-    }
+    };
+    if (full && nt) stores(std::integral_constant<int, 0>{});
+    else if (full) stores(std::integral_constant<int, 1>{});
+    else stores(std::integral_constant<int, 2>{});
   };
 
   using t_ = std::true_type;
