@@ -301,7 +301,12 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmArgs args) {
   // Store this wave's part of output tile `tl` from the accumulators: fp32 -> output type, 8
   // consecutive columns per lane. The lane index is re-read through an opaque move, so the address
   // arithmetic stays here instead of being hoisted into registers held across the K-loop.
-  auto epilogue = [&](const PpTile& tl_in) SPT_INLINE {
+  // With kReads, the 24 fragment reads of the K-tile at ring position p go out between the stores
+  // (one or two after each), so that the reads do not queue behind all sixteen stores; the reads
+  // are then complete on return. Only for 16-bit outputs: with fp32 ones (split-K partial planes)
+  // the accumulators live beside the fragments being read spilled registers.
+  auto epilogue = [&](const PpTile& tl_in, auto reads_c, int p) SPT_INLINE {
+    constexpr bool kReads = decltype(reads_c)::value;
     PpTile tl;
     tl.t = tl_in.t;
     tl.row0 = __builtin_amdgcn_readfirstlane(tl_in.row0);
@@ -335,34 +340,33 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmArgs args) {
         else store8<OUT, true>(vv, rc, m_lane + dm, tl.rows_left, n_lane + dn, N, args.ldc);
         __builtin_amdgcn_sched_barrier(0);
       };
-      if constexpr (MF == 16) {
-        // one store per A block and row e: columns 8c .. 8c+7 come from the FN = 8 B fragments
+      const char *pa = nullptr, *pb = nullptr;
+      if constexpr (kReads) frag_bases(p, pa, pb);
+      // MF = 16: store s is A block j = s/4, row e = s%4, columns 8c .. 8c+7 from the FN = 8 B
+      // fragments. MF = 32: store s is block (i, j) = (s/(2FM), (s/2) mod FM), half h = s%2, whose
+      // elements 8h .. 8h+7 hold columns 32i + 16h + 8(l/32) + 0..7.
+      constexpr int NS = MF == 16 ? FM * 4 : FN * FM * 2;
+      static_for<NS>([&](auto s_c) {
+        constexpr int st = decltype(s_c)::value;
+        float vv[8];
+        if constexpr (MF == 16) {
+          constexpr int j = st / 4, e = st % 4;
 #pragma unroll
-        for (int j = 0; j < FM; ++j) {
+          for (int f = 0; f < FN; ++f) vv[f] = acc[f][j][e];
+          put8(vv, 16 * j + e, 0);
+        } else {
+          constexpr int i = st / (2 * FM), j = (st / 2) % FM, h = st % 2;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float vv[8];
-#pragma unroll
-            for (int f = 0; f < FN; ++f) vv[f] = acc[f][j][e];
-            put8(vv, 16 * j + e, 0);
-          }
+          for (int e = 0; e < 8; ++e) vv[e] = acc[i][j][8 * h + e];
+          put8(vv, 32 * j, 32 * i + 16 * h);
         }
-      } else {
-        // elements 8h .. 8h+7 of a block hold columns 32i + 16h + 8(l/32) + 0..7
-#pragma unroll
-        for (int i = 0; i < FN; ++i) {
-#pragma unroll
-          for (int j = 0; j < FM; ++j) {
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-              float vv[8];
-#pragma unroll
-              for (int e = 0; e < 8; ++e) vv[e] = acc[i][j][8 * h + e];
-              put8(vv, 32 * j, 32 * i + 16 * h);
-            }
-          }
+        if constexpr (kReads) {
+          static_for<NR>([&](auto r_c) {
+            if constexpr (decltype(r_c)::value * NS / NR == st) read_one(r_c, pa, pb);
+          });
         }
-      }
+      });
+      if constexpr (kReads) wait_lgkmcnt0();
     };
     if (full && nt) stores(std::integral_constant<int, 0>{});
     else if (full) stores(std::integral_constant<int, 1>{});
@@ -397,10 +401,16 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmArgs args) {
           if constexpr (!SPLIT) issue_a(nx, a_at(q));
           issue_b(nx, b_at(q));
         }
-        if constexpr (decltype(first_c)::value) {
-          if (prev.t < args.num_tiles) epilogue(prev);
+        if (decltype(first_c)::value && prev.t < args.num_tiles) {
+          if constexpr (OUT == 2) {
+            epilogue(prev, std::false_type{}, 0);
+            read_frags(p);
+          } else {
+            epilogue(prev, std::true_type{}, p);
+          }
+        } else {
+          read_frags(p);
         }
-        read_frags(p);
       } else {
         if (valid(nx)) {
           const OpLoads o = prep_b(nx, b_at(pos_step(p, 1)));
@@ -424,7 +434,7 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmArgs args) {
       prev = cur.tl;
     }
     // phase 2G: the last tile's stores, beside G1's last compute phase
-    epilogue(prev);
+    epilogue(prev, std::false_type{}, 0);
     barrier_sync();
   } else {
     // --------------------------------------------------------------------------- G1
@@ -457,8 +467,16 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmArgs args) {
       };
       if constexpr (kFirst) {
         wait_a();
-        if (prev.t < args.num_tiles) epilogue(prev);
-        read_frags(p);
+        if (prev.t < args.num_tiles) {
+          if constexpr (OUT == 2) {
+            epilogue(prev, std::false_type{}, 0);
+            read_frags(p);
+          } else {
+            epilogue(prev, std::true_type{}, p);
+          }
+        } else {
+          read_frags(p);
+        }
       } else if constexpr (SPLIT) {
         if (valid(n2)) {
           const OpLoads o = prep_a(n2, a_at(pos_step(p, 2)));
@@ -483,7 +501,7 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmArgs args) {
       for (int u = 1; u < KT; ++u) step(f_{});
       prev = cur.tl;
     }
-    epilogue(prev);  // after the last barrier
+    epilogue(prev, std::false_type{}, 0);  // after the last barrier
   }
 }
 
