@@ -26,9 +26,9 @@
 // 2g+1 (G0) and 2g+2 (G1). Loads run ahead into the next unit the same way they run ahead inside
 // one, so there is no prologue per unit: the pages' overlap of the next tile's loads with the
 // current math and the previous tile's stores, carried across tiles.
-// A group stores a finished output tile in its next memory phase, before reading the next
-// fragments; after the last K-tile G0 stores in phase 2G, beside G1's last MFMAs, and G1 after
-// the last barrier. Both groups pass 2G + 2 barriers.
+// A group stores a finished output tile in its next memory phase, with the next K-tile's fragment
+// reads spread between the stores (16-bit outputs); after the last K-tile G0 stores in phase 2G,
+// beside G1's last MFMAs, and G1 after the last barrier. Both groups pass 2G + 2 barriers.
 //
 // Ring, S = 2: two 64 KiB stages (stage g mod 2). In phase 2g G0 loads all of K-tile g+1 and waits
 // for it at the end of phase 2g+1: loads are issued in bursts, every other phase.
