@@ -270,6 +270,29 @@ def test_output_rounding_bit_exact(in_dt, out_dt):
         check_full(a, b, K, in_dt, out_dt, c, N, exact=True)
 
 
+@pytest.mark.parametrize("out_dt", [si.F16, si.F32])
+def test_nonfinite_inputs_propagate(out_dt):
+    # an infinity in A and a NaN in B, among small integers (some zero): the oracle's fp64 sums give
+    # NaN where inf meets 0 or the NaN, ±inf along the rest of inf's row, and exact values elsewhere.
+    # Every kernel family must give NaN where the oracle does, the same infinity, and the same bits
+    M, N, K = 300, 264, 200
+    a = ints(M, K, si.F16, 91)
+    b = ints(N, K, si.F16, 92)
+    a[37, 150] = 0x7C00   # +inf
+    b[101, 7] = 0x7E00    # NaN
+    c_ref, _, _ = orc.gemm(a, b, K, si.F16, out_dt)
+    ref = orc.decode(out_dt, c_ref).astype(np.float64)
+    assert np.isnan(ref[:, 101]).all() and np.isinf(ref[37]).sum() > 0 and np.isnan(ref[37]).sum() > 1
+    for c_cfg in (None, ring_cfg(64, 5, 8), cfg(128, 128, 4), cfg(32, 32, 8, bk=128, waves=2, stream=2),
+                  cfg(128, 128, 2, path=spt.GEMM_LOAD_REG), ring_cfg(64, 5, 8, splits=3), cfg(64, 64, 4, splits=2)):
+        c, _ = run_gpu(a, b, K, si.F16, out_dt, config=c_cfg)
+        got = orc.decode(out_dt, np.ascontiguousarray(c[:, :N])).astype(np.float64)
+        nan = np.isnan(ref)
+        assert np.array_equal(np.isnan(got), nan), c_cfg
+        fin = ~nan
+        assert np.array_equal(got[fin], ref[fin]), c_cfg
+
+
 @pytest.mark.parametrize("K", [1, 8, 63, 64, 65, 127, 128, 129, 200, 256])
 @pytest.mark.parametrize("s", [1, 2, 3, 4])
 def test_k_around_stage_depth(K, s):
