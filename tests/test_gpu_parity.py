@@ -270,6 +270,23 @@ def test_output_rounding_bit_exact(in_dt, out_dt):
         check_full(a, b, K, in_dt, out_dt, c, N, exact=True)
 
 
+@pytest.mark.parametrize("in_dt", [si.F16, si.BF16])
+def test_subnormal_inputs_bit_exact(in_dt):
+    # A entirely subnormal (exponent field 0, random mantissa and sign) against small integers: the
+    # sums are exact in fp32 (bf16 subnormals are fp32 subnormals, so the MFMA must keep denormals),
+    # and every kernel family must equal the oracle bit for bit, in fp32 and in the input type
+    rng = np.random.default_rng(5)
+    M, N, K = 200, 136, 72
+    mbits = 10 if in_dt == si.F16 else 7
+    a = ((rng.integers(0, 2, (M, K)) << 15) | rng.integers(1, 1 << mbits, (M, K))).astype(np.uint16)
+    b = ints(N, K, in_dt, 93)
+    for out_dt in (si.F32, in_dt):
+        for c_cfg in (None, ring_cfg(64, 5, 8), cfg(128, 128, 4), cfg(32, 32, 8, bk=128, waves=2),
+                      cfg(128, 128, 2, path=spt.GEMM_LOAD_REG), ring_cfg(64, 5, 8, splits=3)):
+            c, _ = run_gpu(a, b, K, in_dt, out_dt, config=c_cfg)
+            check_full(a, b, K, in_dt, out_dt, c, N, exact=True)
+
+
 @pytest.mark.parametrize("out_dt", [si.F16, si.F32])
 def test_nonfinite_inputs_propagate(out_dt):
     # an infinity in A and a NaN in B, among small integers (some zero): the oracle's fp64 sums give
