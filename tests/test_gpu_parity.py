@@ -270,6 +270,43 @@ def test_output_rounding_bit_exact(in_dt, out_dt):
         check_full(a, b, K, in_dt, out_dt, c, N, exact=True)
 
 
+def test_concurrent_streams():
+    # one plan without a workspace run on four streams at once, each on its own operands; and matmul,
+    # which keeps one plan per stream, on two streams at once for a shape that splits K (a workspace).
+    # Every result equals the oracle bit for bit
+    M, N, K = 520, 392, 648
+    plan = spt.Plan(M, N, K, torch.float16, torch.float32)
+    assert plan.workspace_bytes() == 0
+    streams = [torch.cuda.Stream() for _ in range(4)]
+    ops = []
+    for i, st in enumerate(streams):
+        a, b = ints(M, K, si.F16, 500 + i), ints(N, K, si.F16, 600 + i)
+        A, B = to_device(a, si.F16), to_device(b, si.F16)
+        C = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+        ops.append((a, b, A, B, C, st))
+    torch.cuda.synchronize()
+    for _ in range(3):
+        for a, b, A, B, C, st in ops:
+            plan.run_ptrs(A.data_ptr(), B.data_ptr(), C.data_ptr(), st.cuda_stream)
+    torch.cuda.synchronize()
+    for a, b, A, B, C, st in ops:
+        check_full(a, b, K, si.F16, si.F32, C.cpu().numpy(), N, exact=True)
+    plan.close()
+    Ms, Ns, Ks = 256, 256, 8192
+    assert spt.Plan(Ms, Ns, Ks, torch.bfloat16, torch.bfloat16).describe()["splits"] > 1
+    outs = []
+    for i, st in enumerate(streams[:2]):
+        a, b = ints(Ms, Ks, si.BF16, 700 + i), ints(Ns, Ks, si.BF16, 800 + i)
+        A, B = to_device(a, si.BF16), to_device(b, si.BF16)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(st):
+            C = spt.matmul(A, B, torch.float32)
+        outs.append((a, b, C))
+    torch.cuda.synchronize()
+    for a, b, C in outs:
+        check_full(a, b, Ks, si.BF16, si.F32, C.cpu().numpy(), Ns, exact=True)
+
+
 @pytest.mark.parametrize("in_dt", [si.F16, si.BF16])
 def test_subnormal_inputs_bit_exact(in_dt):
     # A entirely subnormal (exponent field 0, random mantissa and sign) against small integers: the
