@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <mutex>
 
 #include "gemm.h"
 
@@ -84,7 +85,15 @@ __global__ void __launch_bounds__(256) read16_kernel(const u32x4* __restrict__ s
   if ((acc[0] ^ acc[1] ^ acc[2] ^ acc[3]) == 0x12345678u) sink[0] = 1u;
 }
 
+// One 4-byte sink per device, allocated on the first probe call there; the lock keeps two threads'
+// first calls from both allocating it.
 float* g_sink[64] = {};
+std::mutex g_sink_mu;
+
+bool sink_ready(int dev) {
+  std::lock_guard<std::mutex> lock(g_sink_mu);
+  return g_sink[dev] || hipMalloc(&g_sink[dev], sizeof(float)) == hipSuccess;
+}
 
 }  // namespace
 
@@ -92,7 +101,7 @@ extern "C" gemm_status_t gemm_probe_mfma_peak(int64_t iters, int waves_per_simd,
   if (iters < 1 || waves_per_simd < 1 || waves_per_simd > 2 || !flops) return GEMM_ERR_INVALID;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return GEMM_ERR_HIP;
-  if (!g_sink[dev] && hipMalloc(&g_sink[dev], sizeof(float)) != hipSuccess) return GEMM_ERR_HIP;
+  if (!sink_ready(dev)) return GEMM_ERR_HIP;
   int cu = 0;
   if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return GEMM_ERR_HIP;
   const int grid = cu * waves_per_simd;  // 4 waves per workgroup: one per SIMD
@@ -121,7 +130,7 @@ extern "C" gemm_status_t gemm_probe_lds_read(int swizzle, int64_t iters, void* s
   if (swizzle < -1 || swizzle > 4 || iters < 1) return GEMM_ERR_INVALID;
   int dev = 0, cu = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return GEMM_ERR_HIP;
-  if (!g_sink[dev] && hipMalloc(&g_sink[dev], sizeof(float)) != hipSuccess) return GEMM_ERR_HIP;
+  if (!sink_ready(dev)) return GEMM_ERR_HIP;
   if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return GEMM_ERR_HIP;
   hipLaunchKernelGGL(lds_read_kernel, dim3(cu), dim3(256), 0, (hipStream_t)stream, (unsigned*)g_sink[dev], swizzle,
                      iters);
@@ -134,7 +143,7 @@ extern "C" gemm_status_t gemm_probe_read(const void* src, int64_t bytes, void* s
   if (bytes == 0) return GEMM_OK;
   int dev = 0, cu = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return GEMM_ERR_HIP;
-  if (!g_sink[dev] && hipMalloc(&g_sink[dev], sizeof(float)) != hipSuccess) return GEMM_ERR_HIP;
+  if (!sink_ready(dev)) return GEMM_ERR_HIP;
   if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return GEMM_ERR_HIP;
   const int64_t n = bytes / 16;
   int64_t grid = (n + 255) / 256;
