@@ -650,6 +650,104 @@ def replay_two_groups(KT, S, p, g1_slack=0, g0_late_wait=False, g0_prologue_slac
             wait(1, (p["pp_g1_wait"] if g1_loaded else 0) + g1_slack)
 
 
+def replay_two_group_stream(units, KT, S, p, store_credit=0):
+    """The two-group phase stream over `units` work units of KT K-tiles, run back to back as the
+    kernel runs them (loads run ahead into the next unit; no ring reset between units), with each
+    finished unit's 16 stores per wave issued where the kernel issues them: G0 after its B loads in
+    the first memory phase of the next unit, G1 after its wait in its first memory phase, and both
+    after the last unit. vmcnt counts loads and stores, and a store may complete before or after any
+    load, so each wait is replayed adversarially: the stores complete first, then the oldest loads,
+    until at most n operations are outstanding. store_credit plants a wait that counts the stores as
+    if they completed in order (threshold raised by that many)."""
+    LA, NS = p["la"], 16
+    ops = {0: [], 1: []}          # per group, in issue order: ("L", operand tile) or ("S", None)
+    done = {0: set(), 1: set()}   # indices of completed operations
+    slot_of, read_done = {}, {}
+
+    def slot(h):
+        return h % 5 if S == 5 else (h // 2) % 2 * 2 + h % 2
+
+    def load(g, h, phase):
+        prev = slot_of.get(slot(h))
+        if prev is not None:
+            assert read_done.get(prev // 2, 1 << 30) < phase, f"slot refilled in phase {phase} before K-tile {prev // 2} was read"
+        slot_of[slot(h)] = h
+        ops[g].extend([("L", h)] * LA)
+
+    def store(g):
+        ops[g].extend([("S", None)] * NS)
+
+    def wait(g, n):
+        out = [i for i in range(len(ops[g])) if i not in done[g]]
+        for i in [i for i in out if ops[g][i][0] == "S"] + [i for i in out if ops[g][i][0] == "L"]:
+            if len(ops[g]) - len(done[g]) <= n:
+                break
+            done[g].add(i)
+
+    def is_landed(h):
+        for g in (0, 1):
+            idx = [i for i, (k, x) in enumerate(ops[g]) if k == "L" and x == h]
+            if idx:
+                return all(i in done[g] for i in idx) and slot_of[slot(h)] == h
+        return False
+
+    def check_read(u, phase):
+        for h in (2 * u, 2 * u + 1):
+            assert is_landed(h), f"operand tile {h} read in phase {phase} before it landed"
+
+    G = units * KT
+    load(0, 0, -1)
+    load(0, 1, -1)
+    if S == 5 and G > 1:
+        load(0, 2, -1)
+        wait(0, p["pp_g0_prologue_wait"])
+    else:
+        wait(0, 0)
+    for u in range(G):
+        first = u % KT == 0 and u > 0            # the first K-tile of a unit after the first: epilogue
+        p0, p1 = 2 * u, 2 * u + 1
+        if u + 1 < G:
+            if S == 5:
+                load(0, 2 * (u + 1) + 1, p0)
+            else:
+                load(0, 2 * (u + 1), p0)
+                load(0, 2 * (u + 1) + 1, p0)
+        if first:
+            store(0)
+        check_read(u, p0)
+        g1_loaded = False
+        if S == 5 and u + 2 < G:
+            load(1, 2 * (u + 2), p1)
+            g1_loaded = True
+        if S == 5:
+            wait(1, (p["pp_g1_wait"] if g1_loaded else 0) + (store_credit if any(k == "S" for k, _ in ops[1]) else 0))
+        if first:
+            store(1)
+        check_read(u, p1)
+        read_done[u] = p1
+        wait(0, 0)
+    store(0)
+    store(1)
+
+
+@pytest.mark.parametrize("cfg", TWO_GROUP_KERNELS)
+def test_two_group_stream_with_stores_replay(cfg):
+    p = protocol(cfg)
+    for units in (1, 2, 3):
+        for KT in (1, 2, 3, 5, 8):
+            replay_two_group_stream(units, KT, cfg[3], p)
+
+
+def test_two_group_stream_replay_catches_a_wait_that_trusts_store_order():
+    # a G1 wait that treats the stores issued after A(g+1)'s loads as completing in order (raising its
+    # threshold by their count) lets a read of A(g+1) run before it lands
+    p5 = protocol((256, 256, 64, 5, 8))
+    with pytest.raises(AssertionError, match="before it landed"):
+        for units in (2, 3):
+            for KT in (2, 3, 5):
+                replay_two_group_stream(units, KT, 5, p5, store_credit=16)
+
+
 @pytest.mark.parametrize("cfg", TWO_GROUP_KERNELS)
 def test_two_group_schedule_replay(cfg):
     p = protocol(cfg)
