@@ -499,6 +499,69 @@ def replay_ring(KT, S, p, wait_slack=0, refill_before_barrier=False):
         assert landed(k + 1), f"K-tile {k + 1} read before it landed (KT={KT}, S={S})"
 
 
+def replay_ring_units(units, KT, S, p, store_credit=0):
+    """The 4-wave kernel over `units` work units in a row, as one wave runs them: per unit a prologue,
+    the K-loop and 16 epilogue stores, the ring restarting at slot 0 while the previous unit's
+    zero-filling dummy K-tiles may still be in flight into the same slots. vmcnt counts loads and
+    stores; stores may complete before any load, loads complete in issue order, so every wait is
+    replayed with the stores completing first. A slot's new load may be issued while an older load
+    into it is in flight only because this wave's loads land in order; the check is that every read
+    finds the newest load of its slot landed and that the slot holds the K-tile it reads."""
+    LW, NS = p["lw"], 16
+    ops = []                 # ("L", unit, tile) or ("S",)
+    done = set()
+    holds = {}               # slot -> (unit, tile) of its newest load
+
+    def issue(u, tile, n):
+        holds[tile % S] = (u, tile)
+        ops.extend([("L", u, tile)] * n)
+
+    def wait(n):
+        out = [i for i in range(len(ops)) if i not in done]
+        for i in [i for i in out if ops[i][0] == "S"] + [i for i in out if ops[i][0] == "L"]:
+            if len(ops) - len(done) <= n:
+                break
+            done.add(i)
+
+    def readable(u, tile):
+        idx = [i for i, o in enumerate(ops) if o[0] == "L" and o[1] == u and o[2] == tile]
+        return len(idx) == LW and all(i in done for i in idx) and holds[tile % S] == (u, tile)
+
+    for u in range(units):
+        for t in range(S):
+            issue(u, t, LW)
+        wait(p["prologue_wait"] + (store_credit if u else 0))
+        assert readable(u, 0), f"unit {u}: K-tile 0 read before it landed"
+        for k in range(KT):
+            if k >= 1 and p["refill_later"]:
+                issue(u, k - 1 + S, p["refill_later"])
+            if k + 1 == KT:
+                break
+            if S == 1:
+                issue(u, k + 1, LW)
+                wait(0)
+            else:
+                wait(p["handover_wait"])
+                issue(u, k + S, p["refill_now"])
+            assert readable(u, k + 1), f"unit {u}: K-tile {k + 1} read before it landed"
+        ops.extend([("S",)] * NS)
+
+
+@pytest.mark.parametrize("cfg", PLAIN_KERNELS)
+def test_ring_protocol_replay_over_units_with_stores(cfg):
+    p = protocol(cfg)
+    S = cfg[3]
+    for KT in range(1, 2 * S + 3):
+        replay_ring_units(3, KT, S, p)
+
+
+def test_ring_units_replay_catches_a_wait_that_trusts_store_order():
+    p = protocol((128, 128, 64, 4, 4))
+    with pytest.raises(AssertionError, match="before it landed"):
+        for KT in range(1, 8):
+            replay_ring_units(3, KT, 4, p, store_credit=16)
+
+
 @pytest.mark.parametrize("cfg", PLAIN_KERNELS)
 def test_ring_protocol_replay(cfg):
     p = protocol(cfg)
