@@ -8,7 +8,9 @@
 //   * loads: direct global->LDS buffer loads (buffer_load_dwordx4 ... lds), 64 lanes x 16 B per
 //     instruction, issued by every wave for its share of the tile (there is no single-issuer
 //     copy engine). The XOR swizzle is applied on the source side: lane l of an instruction
-//     lands at LDS byte 16*l, so it fetches the global chunk that belongs there.
+//     lands at LDS byte 16*l, so it fetches the global chunk that belongs there. STREAM = 1 or 2
+//     loads A or B with the non-temporal hint (skinny shapes, where one workgroup reads each
+//     tile of that operand once).
 //   * "full": each wave waits for its own loads with s_waitcnt vmcnt(n) and then s_barrier
 //     publishes every wave's part (a barrier alone does not wait for in-flight loads, just as
 //     a thread barrier cannot see a TMA transfer). "free": each wave drains its ds_reads of a
