@@ -55,7 +55,7 @@ def draw_case(i):
     if rng.random() < 0.85:
         bm, bn, bk, s, w, mf, path = KERNELS[int(rng.integers(0, len(KERNELS)))]
         persistent = int(rng.choice([0, 1, 1, 2]))
-        splits = int(rng.choice([1, 1, 2, 3, 4])) if path == 0 else 1
+        splits = int(rng.choice([1, 1, 2, 3, 4, 7])) if path == 0 else 1
         stream = int(rng.choice([0, 1, 2])) if (bm, w) == (32, 2) else 0
         cfg = dict(bm=bm, bn=bn, bk=bk, stages=s, waves=w, mfma=mf, persistent=persistent, group_m=int(rng.choice([1, 3, 8])),
                    load_path=path, grid=int(rng.integers(1, 8)) if persistent and rng.random() < 0.5 else 0,
