@@ -4,6 +4,8 @@ the HIP kernels.
 """
 from __future__ import annotations
 
+from collections import OrderedDict
+
 import torch
 
 from . import _lib
@@ -67,24 +69,42 @@ class Plan:
             pass
 
 
-_plan_cache: dict = {}
+# matmul's plans, least recently used first. A plan may own a device workspace (staged operands up
+# to 3 GiB, split-K partial planes up to 1 GiB), so the cache is bounded: the oldest plan is freed
+# when a new one would exceed _PLAN_CACHE_MAX, after its device has finished the work it enqueued.
+_PLAN_CACHE_MAX = 64
+_plan_cache: OrderedDict = OrderedDict()
+
+
+def _evict_oldest() -> None:
+    key, plan = _plan_cache.popitem(last=False)
+    torch.cuda.synchronize(key[-2])  # work enqueued with the plan must be done before its workspace goes
+    plan.close()
 
 
 def matmul(A: torch.Tensor, B: torch.Tensor, out_dtype: torch.dtype | None = None, out: torch.Tensor | None = None,
            config: dict | None = None) -> torch.Tensor:
-    """C = A·Bᵀ for device tensors A[M,K], B[N,K] (row-major, unit column stride)."""
+    """C = A·Bᵀ for device tensors A[M,K], B[N,K] (row-major, unit column stride), on A's device and
+    that device's current stream."""
     if A.dim() != 2 or B.dim() != 2 or A.shape[1] != B.shape[1]:
         raise ValueError("A[M,K] and B[N,K] required")
+    if B.device != A.device or (out is not None and out.device != A.device):
+        raise ValueError("A, B and out must be on one device")
     M, K = A.shape
     N = B.shape[0]
     out_dtype = out_dtype or A.dtype
-    C = out if out is not None else torch.empty((M, N), dtype=out_dtype, device=A.device)
-    # a plan with a workspace must not run on two streams at once: one cached plan per stream
-    stream = torch.cuda.current_stream(A.device).cuda_stream
-    key = (M, N, K, A.dtype, out_dtype, A.stride(0), B.stride(0), C.stride(0),
-           tuple(sorted(config.items())) if config else None, A.device.index, stream)
-    plan = _plan_cache.get(key)
-    if plan is None:
-        plan = Plan(M, N, K, A.dtype, out_dtype, A.stride(0), B.stride(0), C.stride(0), config)
-        _plan_cache[key] = plan
-    return plan.run(A, B, C, stream)
+    with torch.cuda.device(A.device):
+        C = out if out is not None else torch.empty((M, N), dtype=out_dtype, device=A.device)
+        # a plan with a workspace must not run on two streams at once: one cached plan per stream
+        stream = torch.cuda.current_stream(A.device).cuda_stream
+        key = (M, N, K, A.dtype, out_dtype, A.stride(0), B.stride(0), C.stride(0),
+               tuple(sorted(config.items())) if config else None, A.device.index, stream)
+        plan = _plan_cache.get(key)
+        if plan is None:
+            plan = Plan(M, N, K, A.dtype, out_dtype, A.stride(0), B.stride(0), C.stride(0), config)
+            while len(_plan_cache) >= _PLAN_CACHE_MAX:
+                _evict_oldest()
+            _plan_cache[key] = plan
+        else:
+            _plan_cache.move_to_end(key)
+        return plan.run(A, B, C, stream)

@@ -270,6 +270,31 @@ def test_output_rounding_bit_exact(in_dt, out_dt):
         check_full(a, b, K, in_dt, out_dt, c, N, exact=True)
 
 
+def test_matmul_plan_cache_is_bounded():
+    # 70 distinct shapes through matmul, some with workspaces (staged operands, split K): the cache
+    # keeps at most its bound of plans, every result equals the oracle, and an evicted shape plans
+    # again and still does
+    from software_pipelined_tiled_amd import torch_api
+    torch_api._plan_cache.clear()
+    cases = []
+    for i in range(70):
+        M, N, K = 40 + 3 * i, 56 + 5 * (i % 7), (64 if i % 3 else 77) + 8 * (i % 5) + (4096 if i % 10 == 0 else 0)
+        a, b = ints(M, K, si.F16, 1000 + i), ints(N, K, si.F16, 2000 + i)
+        A, B = to_device(a, si.F16), to_device(b, si.F16)
+        C = spt.matmul(A, B, torch.float32)
+        assert len(torch_api._plan_cache) <= torch_api._PLAN_CACHE_MAX
+        cases.append((a, b, K, N, C))
+    torch.cuda.synchronize()
+    assert len(torch_api._plan_cache) == torch_api._PLAN_CACHE_MAX
+    for a, b, K, N, C in cases:
+        check_full(a, b, K, si.F16, si.F32, C.cpu().numpy(), N, exact=True)
+    a, b, K, N, _ = cases[0]                       # long evicted: planned again
+    C = spt.matmul(to_device(a, si.F16), to_device(b, si.F16), torch.float32)
+    torch.cuda.synchronize()
+    check_full(a, b, K, si.F16, si.F32, C.cpu().numpy(), N, exact=True)
+    torch_api._plan_cache.clear()
+
+
 def test_concurrent_streams():
     # one plan without a workspace run on four streams at once, each on its own operands; and matmul,
     # which keeps one plan per stream, on two streams at once for a shape that splits K (a workspace).
