@@ -32,6 +32,7 @@ class Plan:
         self.handle = None
         self.handle = _lib.gemm_plan_create(self.M, self.N, self.K, dtype_code(in_dtype), dtype_code(in_dtype),
                                             dtype_code(out_dtype), self.lda, self.ldb, self.ldc, config)
+        self.device = torch.cuda.current_device()  # where the library made the plan and its workspace
 
     def describe(self) -> dict:
         return _lib.gemm_plan_describe(self.handle)
@@ -52,6 +53,8 @@ class Plan:
                                       ("C", C, self.M, self.ldc, self.out_dtype)):
             if not t.is_cuda or t.dtype != dt:
                 raise ValueError(f"{name} must be a {dt} device tensor")
+            if t.device.index != self.device:
+                raise ValueError(f"{name} is on cuda:{t.device.index}, the plan on cuda:{self.device}")
             if rows > 0 and (t.dim() != 2 or t.shape[0] < rows or t.stride(1) != 1 or t.stride(0) != ld):
                 raise ValueError(f"{name} must be [>= {rows}, *] row-major with stride {ld}")
         self.run_ptrs(A.data_ptr(), B.data_ptr(), C.data_ptr(), stream)
