@@ -156,23 +156,33 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmArgs args) {
     b_rd[s] = lds_chunk_offset(BN, TN * wn + lane % MF, (MK / 8) * s + lane / MF);
   }
 
-  // A position in the K-tile stream: an output tile and a K-tile inside it. advance() moves to the
-  // next K-tile, into the next output tile after the last. (All of it is wave-uniform; the loads
-  // re-read it through readfirstlane so that it stays in scalar registers.)
+  // A position in the K-tile stream: an output tile, a K-tile inside it, and the buffer descriptors
+  // of the tile's A rows and B rows. advance() moves to the next K-tile, into the next output tile
+  // after the last. All of it is wave-uniform and lives in scalar registers. The tile change is
+  // kept a branch: if-converted, the raster decode (two divisions) and the 64-bit descriptor
+  // arithmetic ran in every K-tile, and the scalar work a memory phase issues lengthens it (made
+  // once per tile, 2 % faster on 8192^3).
   struct Cursor {
     PpTile tl;
     int u;
+    __amdgpu_buffer_rsrc_t ra, rb;
+  };
+  auto set_rsrc = [&](Cursor& c) SPT_INLINE {
+    c.ra = make_rsrc((const char*)args.A + (size_t)c.tl.row0 * args.lda * 2, ((uint64_t)(c.tl.rows_left - 1) * args.lda + K) * 2);
+    c.rb = make_rsrc((const char*)args.B + (size_t)c.tl.col0 * args.ldb * 2, ((uint64_t)(c.tl.cols_left - 1) * args.ldb + K) * 2);
   };
   auto cursor_at = [&](int t) SPT_INLINE {
     Cursor c;
     c.tl = tile_at(t);
     c.u = 0;
+    set_rsrc(c);
     return c;
   };
   auto advance = [&](Cursor& c) SPT_INLINE {
-    if (++c.u == KT) {
+    if (__builtin_expect(++c.u == KT, 0)) {
       c.u = 0;
       c.tl = tile_at(c.tl.t + args.grid);
+      set_rsrc(c);
     }
   };
   auto valid = [&](const Cursor& c) SPT_INLINE { return c.tl.t < args.num_tiles; };
@@ -181,9 +191,9 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmArgs args) {
   // `dst`. The lane's offset is its row times ld plus its chunk; a row past the matrix edge then
   // lies at or beyond the descriptor's num_records and reads zero. A chunk at or past K is moved
   // beyond num_records explicitly (one select per call); the K offset rides in the scalar offset.
-  // An operand tile's loads, prepared once (descriptor, the lane's offset, the LDS base) and then
-  // issued one instruction at a time, so that a memory phase can spread them between its
-  // fragment reads.
+  // An operand tile's loads, prepared once (the cursor's descriptor, the K offset, the lane's
+  // offset, the LDS base) and then issued one instruction at a time, so that a memory phase can
+  // spread them between its fragment reads.
   struct OpLoads {
     __amdgpu_buffer_rsrc_t r;
     unsigned v0, lds;
@@ -192,9 +202,7 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmArgs args) {
   auto prep_a = [&](const Cursor& c, int dst) SPT_INLINE {
     OpLoads o;
     o.k0 = ktile(__builtin_amdgcn_readfirstlane(c.u)) * BK + __builtin_amdgcn_readfirstlane(c.tl.kb);
-    const int row0 = __builtin_amdgcn_readfirstlane(c.tl.row0);
-    const int rows_left = __builtin_amdgcn_readfirstlane(c.tl.rows_left);
-    o.r = make_rsrc((const char*)args.A + (size_t)row0 * args.lda * 2, ((uint64_t)(rows_left - 1) * args.lda + K) * 2);
+    o.r = c.ra;
     o.v0 = lane_kc < K - o.k0 ? (unsigned)(a_lrow * args.lda + lane_kc) * 2u : kOOB;
     o.lds = smem_base + (unsigned)__builtin_amdgcn_readfirstlane(dst) + LA * v * 1024;
     o.ld = args.lda;
@@ -203,9 +211,7 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmArgs args) {
   auto prep_b = [&](const Cursor& c, int dst) SPT_INLINE {
     OpLoads o;
     o.k0 = ktile(__builtin_amdgcn_readfirstlane(c.u)) * BK + __builtin_amdgcn_readfirstlane(c.tl.kb);
-    const int col0 = __builtin_amdgcn_readfirstlane(c.tl.col0);
-    const int cols_left = __builtin_amdgcn_readfirstlane(c.tl.cols_left);
-    o.r = make_rsrc((const char*)args.B + (size_t)col0 * args.ldb * 2, ((uint64_t)(cols_left - 1) * args.ldb + K) * 2);
+    o.r = c.rb;
     o.v0 = lane_kc < K - o.k0 ? (unsigned)(b_lrow * args.ldb + lane_kc) * 2u : kOOB;
     o.lds = smem_base + (unsigned)__builtin_amdgcn_readfirstlane(dst) + LB * v * 1024;
     o.ld = args.ldb;
@@ -233,8 +239,8 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmArgs args) {
   auto a_at = [&](int p) SPT_INLINE { return SPLIT ? p * A_BYTES : p * STAGE; };
   auto b_at = [&](int p) SPT_INLINE { return SPLIT ? (p + 1 == S ? 0 : p + 1) * A_BYTES : p * STAGE + A_BYTES; };
   auto pos_step = [&](int p, int n) SPT_INLINE {  // ring position of K-tile g+n
-    const int q = SPLIT ? p + 2 * n : p + n;
-    return q % S;
+    const int q = SPLIT ? p + 2 * n : p + n;  // n <= 2, so q < 2S
+    return q >= S ? q - S : q;
   };
 
   u32x4 xf[NSUB][FN], yf[NSUB][FM];  // the K-tile's fragments: B side (x), A side (y)
