@@ -135,3 +135,16 @@ def test_bench_parity_checks_every_row_it_computes():
     bad[37, 11] = si.to_f16_bits(np.array([1000.0], np.float32))[0]
     _, par = bench.cpu_baseline(a, b, K, si.F16, si.F16, bad, seconds=5.0, full_seconds=30.0)
     assert not par["ok"] and par["n_fail"] == 1 and par["worst_index"] == [37, 11]
+
+
+def test_abtest_arguments_and_revision_label(tmp_path):
+    from software_pipelined_tiled_amd import abtest
+    with pytest.raises(SystemExit):
+        abtest.main(["run", "x/libsptgemm.so", "--workloads", "c3,c9"])  # unknown workload, nothing run
+    lib = tmp_path / "libsptgemm.so"
+    lib.write_bytes(b"")
+    assert abtest._revision(str(lib)) == "tree"
+    (tmp_path / "REVISION").write_text("0123456789abcdef0123\n")
+    assert abtest._revision(str(lib)) == "0123456789ab"
+    # every timed workload is one whose shape the bit-exact checks cover with the same plan family
+    assert {(m, n, k) for m, n, k, _ in abtest.WORKLOADS.values()} <= {(m, n, k) for m, n, k, _, _ in abtest.CHECKS}
