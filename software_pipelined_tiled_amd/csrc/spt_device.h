@@ -77,7 +77,10 @@ __device__ __forceinline__ unsigned lds_addr(const void* p) { return (unsigned)(
 // destination with a wait for this load, which serialises fragment reads behind the loads in
 // flight. A kernel using it orders its LDS reads after its own loads explicitly (s_waitcnt vmcnt,
 // then s_barrier) before any wave reads a tile.
-// `lds` is the destination's LDS byte address (wave-uniform).
+// `lds` is the destination's LDS byte address (wave-uniform). hipcc warns that M0, a reserved
+// register, is on the clobber list: the compiler neither saves it around the statement nor knows
+// the value left in it, so a kernel using this must not rely on M0 anywhere else (the compiler's
+// own code included; tests/test_generated_code.py reads the built kernels back and checks that).
 __device__ __forceinline__ void dma16_unseen(__amdgpu_buffer_rsrc_t r, unsigned lds, unsigned voffset,
                                              unsigned soffset) {
   const unsigned m0 = __builtin_amdgcn_readfirstlane(lds);
