@@ -148,3 +148,15 @@ def test_abtest_arguments_and_revision_label(tmp_path):
     assert abtest._revision(str(lib)) == "0123456789ab"
     # every timed workload is one whose shape the bit-exact checks cover with the same plan family
     assert {(m, n, k) for m, n, k, _ in abtest.WORKLOADS.values()} <= {(m, n, k) for m, n, k, _, _ in abtest.CHECKS}
+
+
+def test_timeline_instruments_the_current_kernel():
+    # the timeline tool's source transform still finds its anchors in the kernel as it stands: one
+    # recorder, and a timestamp after each of the eight barriers of the phase stream
+    from software_pipelined_tiled_amd import timeline
+    src = open(os.path.join(ROOT, "software_pipelined_tiled_amd", "csrc", "spt_gemm_pp.hip")).read()
+    out = timeline.instrument(src)
+    assert out.count("barrier_sync(); rec();") == 8 and out.count("rec();") == 9
+    assert "spt_timeline_read" in out and src.count("rec()") == 0
+    with pytest.raises(ValueError):
+        timeline.instrument(src.replace("barrier_sync();", "", 1))
