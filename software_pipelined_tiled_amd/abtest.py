@@ -1,4 +1,4 @@
-"""Same-box comparison of library builds from different revisions of this repository.
+"""Same-GPU comparison of library builds from different revisions of this repository.
 
     python -m software_pipelined_tiled_amd.abtest build REV OUTDIR
         (CPU) extracts the sources of git revision REV and builds them with that revision's own
@@ -12,8 +12,8 @@
         runs of 10; the best and the mean of the three, TFLOP/s). One line per library and round.
 
 The libraries must share the C ABI of the binding in this tree (the shape of gemm_config_t and the
-entry points' signatures). The boxes' clocks differ by up to 15 %, so only builds compared within one
-call, alternated, say anything about each other.
+entry points' signatures). Under this load the clock one GPU holds differs from another's by up to 15 %, so
+only builds alternated on one GPU in one sequence say anything about each other.
 """
 from __future__ import annotations
 
