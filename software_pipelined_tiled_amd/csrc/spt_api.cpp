@@ -147,7 +147,7 @@ int pick_splits(const gemm_config_t& c, int64_t M, int64_t N, int64_t K, int cu_
   if (!is_dma(c.load_path) || K == 0) return 1;
   const int64_t tiles = ceil_div(M, c.bm) * ceil_div(N, c.bn);
   const int64_t slots = (int64_t)cu_count * groups_per_cu(c, lds_bytes);
-  if (tiles >= slots) return 1;
+  if (tiles == 0 || tiles >= slots) return 1;  // no output (M or N is 0): nothing to split
   const int64_t kt = ceil_div(K, c.bk);
   int64_t s = slots / tiles;
   if (s > kt / kMinKtPerSplit) s = kt / kMinKtPerSplit;

@@ -402,6 +402,24 @@ def test_k_zero_writes_zeros():
         assert np.all(c[:, :40] == 0)
 
 
+def test_empty_output_is_a_no_op():
+    # M or N = 0 with K > 0: plan creation and the run succeed and write nothing (a regression: the
+    # split choice divided by the zero tile count), through the plan and the no-allocation entry point
+    K = 64
+    for M, N in ((0, 37), (37, 0), (0, 0)):
+        A = torch.ones((max(M, 1), K), dtype=torch.float16, device="cuda")
+        B = torch.ones((max(N, 1), K), dtype=torch.float16, device="cuda")
+        C = torch.full((max(M, 1), max(N, 1)), 7.0, dtype=torch.float16, device="cuda")
+        p = spt.Plan(M, N, K, torch.float16, torch.float16, lda=K, ldb=K, ldc=max(N, 1))
+        p.run_ptrs(A.data_ptr(), B.data_ptr(), C.data_ptr())
+        st = spt.lib().gemm_run_noalloc(M, N, K, 0, 0, 0, K, K, max(N, 1), A.data_ptr(), B.data_ptr(),
+                                        C.data_ptr(), None)
+        torch.cuda.synchronize()
+        p.close()
+        assert st == 0
+        assert bool((C == 7.0).all()), (M, N)
+
+
 def test_padded_ld_and_no_out_of_bounds_writes():
     M, N, K = 200, 136, 192
     for in_dt in (si.F16, si.BF16):

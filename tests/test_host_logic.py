@@ -56,6 +56,11 @@ def test_status_strings():
     ((8, 8, 8, F16, F16, F16, 2 ** 31, 8, 8), UNSUPPORTED),
     ((8, 8, 8, F16, F16, F16, 8, 8, 8), OK),
     ((0, 0, 0, F16, F16, F16, 1, 1, 1), OK),              # empty problem
+    ((0, 5, 64, F16, F16, F16, 64, 64, 5), OK),           # no output rows, K > 0 (no split of zero tiles)
+    ((5, 0, 64, F16, F16, F16, 64, 64, 1), OK),           # no output columns
+    ((0, 0, 64, BF16, BF16, F32, 64, 64, 1), OK),
+    ((0, 300, 63, F16, F16, F16, 63, 63, 300), OK),       # staged path (K not a multiple of 8)
+    ((7, 0, 4096, F16, F16, F16, 4100, 4100, 1), OK),     # staged path through ld
 ])
 def test_argument_checks(args, status):
     assert spt.gemm_select_config_status(*args) == status
@@ -830,3 +835,13 @@ def test_two_group_replay_catches_planted_mistakes():
     with pytest.raises(AssertionError, match="before it landed"):
         for KT in range(1, 12):
             replay_two_groups(KT, 2, p2, g0_late_wait=True)
+
+
+@pytest.mark.parametrize("M,N,K", [(0, 5, 64), (5, 0, 64), (0, 0, 1), (0, 4096, 8192), (8192, 0, 28672)])
+def test_empty_output_plans_on_every_path(M, N, K):
+    # M or N = 0 with K > 0 is a no-op; the choice must not divide by the zero tile count on any path
+    for lda in (K, K + 1, K + 8):
+        for cu, lds in ((256, 160 * 1024), (1, 65536)):
+            assert spt.gemm_select_config_status(M, N, K, F16, F16, F16, lda, lda, max(N, 1), cu, lds) == OK
+            c = spt.gemm_select_config(M, N, K, F16, F16, F16, lda, lda, max(N, 1), cu, lds)
+            assert c["grid"] >= 1 and c["splits"] == 1
