@@ -43,6 +43,7 @@ namespace {
 constexpr int kMaxLds = 160 * 1024;
 constexpr int kGfx950Cus = 256;  // MI355X
 constexpr int kMaxSplits = 16;
+constexpr int64_t kMaxCutRounds = 16;  // rounds of tiles beyond which no two-part cut is tried
 constexpr int kMinKtPerSplit = 8;                           // K-tiles a split-K unit keeps at least
 constexpr int64_t kMaxPartialBytes = (int64_t)1 << 30;      // fp32 partial planes of a split-K plan
 constexpr int64_t kMaxStageBytes = (int64_t)3 << 30;        // staged copies of A and B
@@ -321,7 +322,9 @@ bool choose_parts(int64_t M, int64_t N, int64_t K, int cu_count, int lds_bytes, 
     cfg.lds_bytes = ring_bytes(cfg);
     const int64_t tm = ceil_div(M, c.bm), tn = ceil_div(N, c.bn), T = tm * tn;
     const int64_t G = (int64_t)cu_count * groups_per_cu(cfg, lds_bytes);
-    if (T <= G || T % G == 0) continue;
+    // a cut only pays for the idle part of the last round; past kMaxCutRounds rounds that is under the
+    // 10 % the cut must save, and the search over the rounds would only cost host time
+    if (T <= G || T % G == 0 || T / G > kMaxCutRounds) continue;
     for (int dim = 1; dim >= 0; --dim) {
       for (int64_t k = 1; k <= T / G; ++k) {
         const int64_t lines = dim == 1 ? (k * G) / tm : (k * G) / tn;  // tile columns (rows) of part 0
@@ -355,6 +358,9 @@ void finish_config(gemm_config_t& c, int64_t M, int64_t N, int cu_count, int lds
   const int64_t units = (int64_t)tm * tn * c.splits;
   c.lds_bytes = ring_bytes(c);
   if (c.group_m < 1) c.group_m = 8;
+  // a band of group_m tile rows taller than the grid orders the tiles exactly as one of tm rows; the
+  // clamp also keeps group_m * tn, which the raster computes in 32 bits, within tm * tn
+  if (tm >= 1 && c.group_m > tm) c.group_m = tm;
   if (c.persistent) {
     int64_t g = c.grid > 0 ? c.grid : (int64_t)cu_count * groups_per_cu(c, lds_bytes);
     if (g > units) g = units;
@@ -410,8 +416,10 @@ gemm_status_t select_impl(int64_t M, int64_t N, int64_t K, gemm_dtype_t a, gemm_
   } else {
     cfg = choose(M, N, K, kRegMenu, kRegMenuSize, GEMM_LOAD_REG, cu_count, lds_bytes);
   }
+  const int group_m_in = cfg.group_m < 1 ? 8 : cfg.group_m;  // before the clamp to this tile grid
   int tm, tn;
   finish_config(cfg, M, N, cu_count, lds_bytes, tm, tn);
+  if ((int64_t)tm * tn * cfg.splits > INT32_MAX) return GEMM_ERR_UNSUPPORTED;  // units are numbered in 32 bits
   // the mainloop reads staged operands with rows of kp elements, and a split run writes fp32
   // planes with rows of ldw elements
   const WsLayout w = ws_layout(M, N, K, cfg.load_path, cfg.splits);
@@ -423,8 +431,9 @@ gemm_status_t select_impl(int64_t M, int64_t N, int64_t K, gemm_dtype_t a, gemm_
   if (out_reg) {
     gemm_config_t r = choose(M, N, K, kRegMenu, kRegMenuSize, GEMM_LOAD_REG, cu_count, lds_bytes);
     r.persistent = cfg.persistent;
-    r.group_m = cfg.group_m;
+    r.group_m = group_m_in;
     finish_config(r, M, N, cu_count, lds_bytes, tm, tn);
+    if ((int64_t)tm * tn > INT32_MAX) return GEMM_ERR_UNSUPPORTED;
     if (!offsets_fit(r, lda, ldb, ldc, c)) return GEMM_ERR_UNSUPPORTED;
     *out_reg = r;
   }
@@ -852,6 +861,7 @@ int gemm_schedule_tile(int64_t tiles_m, int64_t tiles_n, int splits, int group_m
   if (tiles_m * tiles_n * splits > INT32_MAX) return -1;
   const int64_t t = (int64_t)round * grid + spt::xcd_remap(wg, grid);
   if (t >= tiles_m * tiles_n * splits) return 0;
+  if (group_m > tiles_m) group_m = (int)tiles_m;  // the same order; keeps group_m * tiles_n in 32 bits
   int m, n, s;
   spt::unit_decode((int)t, (int)tiles_m, (int)tiles_n, group_m, m, n, s);
   *tm = m;
