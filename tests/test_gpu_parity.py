@@ -402,6 +402,24 @@ def test_k_zero_writes_zeros():
         assert np.all(c[:, :40] == 0)
 
 
+@pytest.mark.parametrize("conf", [
+    cfg(128, 128, 4, group_m=1 << 30),                     # band taller than the grid: clamped to its rows
+    cfg(128, 128, 4, group_m=1 << 30, persistent=0),
+    cfg(128, 128, 4, grid=1),                              # one workgroup walks every tile
+    cfg(128, 128, 4, grid=1 << 30),                        # more workgroups than tiles: trimmed
+    cfg(256, 256, 5, waves=8, group_m=1 << 30, grid=1),    # the two-group phase stream over every tile
+    cfg(256, 256, 5, waves=8, grid=1, splits=3),
+    cfg(64, 64, 4, persistent=2, grid=1),                  # dynamic queue with a single workgroup
+])
+def test_override_extremes_bit_exact(conf):
+    M, N, K = 700, 900, 448
+    a = si.make_matrix(M, K, si.BF16, "small_int", 41)
+    b = si.make_matrix(N, K, si.BF16, "small_int", 42)
+    c, desc = run_gpu(a, b, K, si.BF16, si.BF16, config=conf)
+    check_full(a, b, K, si.BF16, si.BF16, c, N, exact=True)
+    assert 1 <= desc["group_m"] <= -(-M // conf["bm"]) and desc["grid"] >= 1
+
+
 def test_empty_output_is_a_no_op():
     # M or N = 0 with K > 0: plan creation and the run succeed and write nothing (a regression: the
     # split choice divided by the zero tile count), through the plan and the no-allocation entry point
