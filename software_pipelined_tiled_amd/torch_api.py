@@ -49,14 +49,17 @@ class Plan:
         _lib.gemm_run(self.handle, a_ptr, b_ptr, c_ptr, stream)
 
     def run(self, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, stream: int | None = None) -> torch.Tensor:
-        for name, t, rows, ld, dt in (("A", A, self.M, self.lda, self.in_dtype), ("B", B, self.N, self.ldb, self.in_dtype),
-                                      ("C", C, self.M, self.ldc, self.out_dtype)):
+        # the kernels touch rows x cols elements at row stride ld from each base pointer
+        for name, t, rows, cols, ld, dt in (("A", A, self.M, self.K, self.lda, self.in_dtype),
+                                            ("B", B, self.N, self.K, self.ldb, self.in_dtype),
+                                            ("C", C, self.M, self.N, self.ldc, self.out_dtype)):
             if not t.is_cuda or t.dtype != dt:
                 raise ValueError(f"{name} must be a {dt} device tensor")
             if t.device.index != self.device:
                 raise ValueError(f"{name} is on cuda:{t.device.index}, the plan on cuda:{self.device}")
-            if rows > 0 and (t.dim() != 2 or t.shape[0] < rows or t.stride(1) != 1 or t.stride(0) != ld):
-                raise ValueError(f"{name} must be [>= {rows}, *] row-major with stride {ld}")
+            if rows > 0 and cols > 0 and (t.dim() != 2 or t.shape[0] < rows or t.shape[1] < cols or t.stride(1) != 1
+                                          or t.stride(0) != ld):
+                raise ValueError(f"{name} must be [>= {rows}, >= {cols}] row-major with row stride {ld}")
         self.run_ptrs(A.data_ptr(), B.data_ptr(), C.data_ptr(), stream)
         return C
 

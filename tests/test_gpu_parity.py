@@ -295,6 +295,28 @@ def test_matmul_plan_cache_is_bounded():
     torch_api._plan_cache.clear()
 
 
+def test_binding_rejects_views_the_kernels_would_overrun():
+    # a view narrower than the plan's K (A, B) or N (C) with the plan's row stride: the kernels would
+    # read or write past it, so the binding refuses it before any launch; the exact views run
+    M, N, K = 64, 48, 96
+    base_a = torch.zeros((M, K + 32), dtype=torch.float16, device="cuda")
+    base_b = torch.zeros((N, K + 32), dtype=torch.float16, device="cuda")
+    base_c = torch.full((M, N + 16), 5.0, dtype=torch.float16, device="cuda")
+    p = spt.Plan(M, N, K, torch.float16, torch.float16, K + 32, K + 32, N + 16)
+    with pytest.raises(ValueError):
+        p.run(base_a[:, :K - 1], base_b[:, :K], base_c[:, :N])
+    with pytest.raises(ValueError):
+        p.run(base_a[:, :K], base_b[:, :K - 8], base_c[:, :N])
+    with pytest.raises(ValueError):
+        p.run(base_a[:, :K], base_b[:, :K], base_c[:, :N - 1])
+    with pytest.raises(ValueError):
+        spt.matmul(base_a[:, :K], base_b[:, :K], out=base_c[:, :N - 1])
+    p.run(base_a[:, :K], base_b[:, :K], base_c[:, :N])
+    torch.cuda.synchronize()
+    p.close()
+    assert bool((base_c[:, :N] == 0).all()) and bool((base_c[:, N:] == 5.0).all())
+
+
 def test_concurrent_streams():
     # one plan without a workspace run on four streams at once, each on its own operands; and matmul,
     # which keeps one plan per stream, on two streams at once for a shape that splits K (a workspace).
