@@ -141,7 +141,8 @@ gemm_status_t gemm_plan_create(gemm_plan_t* out, int64_t M, int64_t N, int64_t K
  *   A: M rows of lda elements, B: N rows of ldb elements, C: M rows of ldc elements; only
  *   C[i*ldc + j] with i < M, j < N is written (the ldc padding is never touched).
  *   If A or B is not 16-byte aligned the register-staged path runs instead of the DMA path
- *   (a staged plan copies the operands and needs no alignment).
+ *   (a staged plan copies the operands and needs no alignment). C needs only its element's
+ *   alignment (2 bytes for F16/BF16, 4 for F32): the 16-byte stores take any byte offset.
  *   A staged plan launches the staging copy first; a split plan launches the mainloop into its
  *   partial planes and then the reduction, all on `stream`.
  * Errors: GEMM_ERR_INVALID (null plan; null A, B or C while M, N > 0), GEMM_ERR_HIP (launch).

@@ -483,6 +483,40 @@ def test_misaligned_pointers_use_register_path():
     check_full(a, b, K, si.F16, si.F32, c, N, exact=True)
 
 
+@pytest.mark.parametrize("conf,out_dt", [
+    (cfg(256, 256, 5, waves=8), si.BF16),                     # the two-group kernel
+    (None, si.BF16),                                          # the built-in choice (32x32 ring tiles)
+    (cfg(128, 128, 4), si.BF16),                              # the ring kernel
+    (cfg(64, 64, 2, path=spt.GEMM_LOAD_REG), si.F16),         # the register-staged kernel
+    (cfg(256, 256, 5, waves=8, splits=3), si.BF16),           # split K: the reduction writes C
+    (None, si.F32),
+])
+@pytest.mark.parametrize("c_off", [1, 3])
+def test_misaligned_output_pointer(conf, out_dt, c_off):
+    # C's base 2 (f16/bf16) or 4 (f32) bytes off a 16-byte boundary, inside a larger NaN-filled
+    # buffer: every output equals the oracle and nothing before or after C, or in its ldc padding,
+    # is written
+    M, N, K, ldc = 520, 300, 192, 310
+    a = ints(M, K, si.BF16 if out_dt != si.F16 else si.F16, 71)
+    b = ints(N, K, si.BF16 if out_dt != si.F16 else si.F16, 72)
+    in_dt = si.BF16 if out_dt != si.F16 else si.F16
+    A, B = to_device(a, in_dt), to_device(b, in_dt)
+    odt = TORCH_DT[out_dt]
+    guard = 128                                               # elements before C (more than 16 bytes)
+    buf = torch.full((guard + c_off + M * ldc + guard,), float("nan"), dtype=odt, device="cuda")
+    C = buf[guard + c_off: guard + c_off + M * ldc].view(M, ldc)
+    assert C.data_ptr() % 16 != 0
+    p = spt.Plan(M, N, K, TORCH_DT[in_dt], odt, K, K, ldc, conf)
+    p.run_ptrs(A.data_ptr(), B.data_ptr(), C.data_ptr())
+    torch.cuda.synchronize()
+    p.close()
+    out = C.cpu()
+    got = out.numpy() if out_dt == si.F32 else out.view(torch.int16).numpy().view(np.uint16)
+    check_full(a, b, K, in_dt, out_dt, got, N, exact=True)
+    rest = torch.cat([buf[:guard + c_off], buf[guard + c_off + M * ldc:], C[:, N:].reshape(-1)])
+    assert bool(torch.isnan(rest.float()).all()), "written outside C"
+
+
 def test_deterministic_and_grouping_invariant():
     M, N, K = 520, 700, 448
     a = si.make_matrix(M, K, si.BF16, "normal_scaled", 41, k_for_scale=K)
