@@ -24,7 +24,8 @@
  *     A and B with rows of roundup(K, 8) elements); otherwise it holds no device memory.
  *     gemm_plan_workspace_bytes reports the size.
  *   - A, B and C are caller-owned device pointers; they must stay valid until the work enqueued
- *     by gemm_run has completed on its stream.
+ *     by gemm_run has completed on its stream. C must not overlap A or B (they are read while C
+ *     is written); A and B are only read and may overlap, or be one matrix (C = A·Aᵀ).
  *   - gemm_run only enqueues kernels on `stream` (a hipStream_t; NULL is the default stream). It
  *     neither allocates nor synchronises. A plan without a workspace may be run concurrently on
  *     several streams; runs of a plan with a workspace share it and must not overlap (run them on

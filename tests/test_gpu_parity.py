@@ -517,6 +517,21 @@ def test_misaligned_output_pointer(conf, out_dt, c_off):
     assert bool(torch.isnan(rest.float()).all()), "written outside C"
 
 
+def test_a_and_b_may_be_one_matrix():
+    # C = A·Aᵀ with both operand pointers on one allocation, through the two-group kernel, the
+    # built-in choice and a split-K plan: the result is the oracle's, bit for bit
+    M, K = 600, 320
+    a = ints(M, K, si.BF16, 81)
+    A = to_device(a, si.BF16)
+    for conf in (cfg(256, 256, 5, waves=8), None, cfg(256, 256, 5, waves=8, splits=2)):
+        C = torch.empty((M, M), dtype=torch.float32, device="cuda")
+        p = spt.Plan(M, M, K, torch.bfloat16, torch.float32, K, K, M, conf)
+        p.run_ptrs(A.data_ptr(), A.data_ptr(), C.data_ptr())
+        torch.cuda.synchronize()
+        p.close()
+        check_full(a, a, K, si.BF16, si.F32, C.cpu().numpy(), M, exact=True)
+
+
 def test_deterministic_and_grouping_invariant():
     M, N, K = 520, 700, 448
     a = si.make_matrix(M, K, si.BF16, "normal_scaled", 41, k_for_scale=K)
