@@ -92,6 +92,22 @@ def test_ring_configs_k_around_depth(K, bk, s, waves):
     check_full(a, b, K, si.BF16, si.F32, c, N, exact=True)
 
 
+@pytest.mark.parametrize("K", [8, 64, 72, 136, 200])
+@pytest.mark.parametrize("s,mfma", [(5, 16), (2, 16), (5, 32)])
+@pytest.mark.parametrize("out_dt", [si.F16, si.BF16])
+def test_two_group_16bit_epilogue_across_tiles_at_small_k(K, s, mfma, out_dt):
+    # the two-group kernel stores a finished tile in the next tile's first memory phase, its fragment
+    # reads spread between the stores (16-bit outputs); with one to four K-tiles per tile and five
+    # tiles per workgroup, the stores, reads and loads of neighbouring tiles meet in every phase
+    M, N = 600, 560
+    in_dt = si.F16 if out_dt == si.F16 else si.BF16
+    a = ints(M, K, in_dt, 900 + K + s)
+    b = ints(N, K, in_dt, 901 + K + mfma)
+    c, desc = run_gpu(a, b, K, in_dt, out_dt, config=ring_cfg(64, s, 8, grid=2, mfma=mfma))
+    assert (desc["waves"], desc["stages"], desc["grid"]) == (8, s, 2)
+    check_full(a, b, K, in_dt, out_dt, c, N, exact=True)
+
+
 # (bm, bn, bk, stages) of 4-wave configurations whose ring leaves room for the dynamic queue's slot
 QUEUE_CONFIGS = [(256, 256, 64, 2), (256, 128, 64, 3), (128, 128, 64, 4), (64, 64, 64, 4), (64, 64, 128, 4)]
 
