@@ -113,15 +113,6 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmArgs args) {
   };
 
   const int u0 = xcd_remap(blockIdx.x, args.grid);
-  // The workgroups of XCD x take the K-tiles of every unit in a rotated order, starting at K-tile
-  // x*KT/8: all workgroups of one XCD stay at the same K position (their L2 sharing is unchanged),
-  // while at any moment the eight XCDs fetch eight different K-slices of the operand bands rather
-  // than the same addresses at once. Only the summation order changes; the epilogues do not move.
-  const int krot = (int)((blockIdx.x % kNumXcd) * KT / kNumXcd);
-  auto ktile = [&](int u) SPT_INLINE {
-    const int r = u + krot;
-    return r < KT ? r : r - KT;
-  };
   if (KT == 0) {  // empty sum: C = 0 (no barriers: every wave takes this branch)
     const float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int t = u0; t < args.num_tiles; t += args.grid) {
@@ -201,7 +192,7 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmArgs args) {
   };
   auto prep_a = [&](const Cursor& c, int dst) SPT_INLINE {
     OpLoads o;
-    o.k0 = ktile(__builtin_amdgcn_readfirstlane(c.u)) * BK + __builtin_amdgcn_readfirstlane(c.tl.kb);
+    o.k0 = __builtin_amdgcn_readfirstlane(c.u) * BK + __builtin_amdgcn_readfirstlane(c.tl.kb);
     o.r = c.ra;
     o.v0 = lane_kc < K - o.k0 ? (unsigned)(a_lrow * args.lda + lane_kc) * 2u : kOOB;
     o.lds = smem_base + (unsigned)__builtin_amdgcn_readfirstlane(dst) + LA * v * 1024;
@@ -210,7 +201,7 @@ __global__ void __launch_bounds__(512, 1) gemm_pp_kernel(GemmArgs args) {
   };
   auto prep_b = [&](const Cursor& c, int dst) SPT_INLINE {
     OpLoads o;
-    o.k0 = ktile(__builtin_amdgcn_readfirstlane(c.u)) * BK + __builtin_amdgcn_readfirstlane(c.tl.kb);
+    o.k0 = __builtin_amdgcn_readfirstlane(c.u) * BK + __builtin_amdgcn_readfirstlane(c.tl.kb);
     o.r = c.rb;
     o.v0 = lane_kc < K - o.k0 ? (unsigned)(b_lrow * args.ldb + lane_kc) * 2u : kOOB;
     o.lds = smem_base + (unsigned)__builtin_amdgcn_readfirstlane(dst) + LB * v * 1024;
