@@ -32,6 +32,8 @@ WORKLOADS = {  # name: (M, N, K, input and output type)
     "c2": (4096, 4096, 4096, "f16"),
     "c3": (8192, 8192, 8192, "bf16"),
     "c4": (16384, 16384, 1024, "bf16"),
+    "c5a": (32, 8192, 8192, "f16"),
+    "c5b": (4093, 5119, 3071, "f16"),
     "c5c": (8192, 1024, 28672, "f16"),
 }
 # (M, N, K, input type, output type): the two-group kernel with full and edge tiles and several rounds,
