@@ -3,7 +3,8 @@ and output types, and every kernel of the tables forced through the configuratio
 built-in choice), with the persistent mode, grid, split count and streaming hint drawn at random.
 
 Operands are small integers, so every fp32 partial sum is exact and each case must equal the oracle
-bit for bit; the ldc padding of C, filled with NaN before the run, must come back untouched. Each
+bit for bit; the ldc padding of C, filled with NaN before the run, must come back untouched. A further
+100 cases of the same draw take N(0,1)/sqrt(K) operands and are held to the oracle's tolerance. Each
 case is a test of its own, named by its index; the index seeds its draw, so a failure can be rerun
 alone with the same inputs.
 """
@@ -92,3 +93,19 @@ def test_random_case_bit_exact(case):
         exp_all_ones = ((dec >> 10) & 31) == 31 if out_dt == si.F16 else ((dec >> 7) & 255) == 255
         man = dec & (1023 if out_dt == si.F16 else 127)
         assert (exp_all_ones & (man != 0)).all()
+
+
+N_REAL_CASES = 100
+
+
+@pytest.mark.parametrize("case", range(N_REAL_CASES))
+def test_random_case_real_values_within_tolerance(case):
+    # the same draw of shapes and configurations (other seeds), with N(0,1)/sqrt(K) operands: every
+    # output within the oracle's bound |C - C_ref| <= 2e-3 (|A||B|^T) + 1 ulp
+    M, N, K, lda, ldb, ldc, in_dt, out_dt, cfg = draw_case(10_000 + case)
+    print(f"real case {case}: M={M} N={N} K={K} lda={lda} ldb={ldb} ldc={ldc} in={in_dt} out={out_dt} config={cfg}",
+          flush=True)
+    a = si.make_matrix(M, K, in_dt, "normal_scaled", 7000 + 2 * case, ld=lda, k_for_scale=K)
+    b = si.make_matrix(N, K, in_dt, "normal_scaled", 7001 + 2 * case, ld=ldb, k_for_scale=K)
+    c, _ = run_gpu(a, b, K, in_dt, out_dt, ldc=ldc, config=cfg)
+    check_full(a, b, K, in_dt, out_dt, c, N)
