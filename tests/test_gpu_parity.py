@@ -458,6 +458,26 @@ def test_override_extremes_bit_exact(conf):
     assert 1 <= desc["group_m"] <= -(-M // conf["bm"]) and desc["grid"] >= 1
 
 
+def test_run_rejects_null_operands():
+    # a null A, B or C for a non-empty problem is GEMM_ERR_INVALID from both entry points, before any
+    # launch; with K = 0 the operands are not read, so only C is required (it is zeroed)
+    lib = spt.lib()
+    M, N, K = 64, 48, 64
+    A = torch.zeros((M, K), dtype=torch.float16, device="cuda")
+    B = torch.zeros((N, K), dtype=torch.float16, device="cuda")
+    C = torch.full((M, N), 3.0, dtype=torch.float16, device="cuda")
+    p = spt.Plan(M, N, K, torch.float16, torch.float16)
+    for a, b, c in ((None, B.data_ptr(), C.data_ptr()), (A.data_ptr(), None, C.data_ptr()), (A.data_ptr(), B.data_ptr(), None)):
+        assert lib.gemm_run(p.handle, a, b, c, None) == spt._lib.GEMM_ERR_INVALID
+        assert lib.gemm_run_noalloc(M, N, K, 0, 0, 0, K, K, N, a, b, c, None) == spt._lib.GEMM_ERR_INVALID
+    p.close()
+    p0 = spt.Plan(M, N, 0, torch.float16, torch.float16, lda=1, ldb=1, ldc=N)
+    assert lib.gemm_run(p0.handle, None, None, C.data_ptr(), None) == 0
+    torch.cuda.synchronize()
+    p0.close()
+    assert bool((C == 0).all())
+
+
 def test_empty_output_is_a_no_op():
     # M or N = 0 with K > 0: plan creation and the run succeed and write nothing (a regression: the
     # split choice divided by the zero tile count), through the plan and the no-allocation entry point
